@@ -1,0 +1,258 @@
+/*
+ * qsa_oracle.c -- CPU oracle for explicit-selection attention and causal scores.
+ *
+ * TEST INFRASTRUCTURE ONLY. Only the tests, the smoke check and the CPU-baseline
+ * leg of the benchmark load this file's library. The product path never calls it
+ * and shares no code, header, table or helper with it.
+ *
+ * It is plain, slow and sequential on purpose: every sum runs in index order,
+ * every value is an IEEE binary64 double, and it is compiled without
+ * contraction (-ffp-contract=off) or fast-math. The pages name an fp32
+ * reference; this oracle works in fp64 so that its own rounding stays far below
+ * the tolerances the GPU path is held to.
+ *
+ * What is computed, and the passages it follows:
+ *
+ *  qso_attn_chunks -- per query token t (cache position p = pos0 + t), per
+ *    64-slot chunk k of the token's id row, per head h:
+ *      valid slots   : ids with 0 <= id < n_cells; -1 marks a slot that
+ *                      contributes nothing ("round 11 track b: qsa attention and
+ *                      score", section "boundaries and provenance": implicit
+ *                      rows poison ids with -1; section "implementation and
+ *                      evaluator": incomplete 64-cell chunks);
+ *      dequantise    : k_d = kq[c][d] * ksc[c][d/32], v_d = vq[c][d] * vsc[c][d/32]
+ *                      (int8 rows, one fp16 scale per 32-dim group; same page,
+ *                      section "implementation and evaluator": four scale
+ *                      groups per K row);
+ *      scaled dot    : S_j = scale * sum_d q[t][h][d] * k_d;
+ *      chunk record  : m = max_j S_j, p_j = exp(S_j - m), l = sum_j p_j,
+ *                      o[d] = sum_j p_j * v_{c_j, d}; a chunk with no valid slot
+ *                      gets m = -inf, l = +0 and its o is left as it was
+ *                      ("round 5 track b: cached residual norms and fused mtp
+ *                      attention", section "mtp attention": per-64-cell chunk
+ *                      arithmetic, per-chunk maxima and denominators).
+ *  qso_merge -- max-first merge of a token's chunk records per head
+ *    (same page and section: "max-first chunk merge"):
+ *      M = max_k m_k over chunks with m_k != -inf, w_k = exp(m_k - M),
+ *      L = sum_k w_k l_k, O[d] = sum_k w_k o_k[d], out = O / L,
+ *      fp16 by round-to-nearest-even. A token with no valid slot gets +0.
+ *  qso_score -- causal scores ("round 11 track b: qsa attention and score",
+ *    sections "implementation and evaluator" and "score: valid negative
+ *    result"): scores[t][c] = scale * sum_h sum_d q[t][h][d] * k[c][d] for
+ *    c <= p; the rest of the 64-cell tile that holds cell p (and lies inside
+ *    the row) gets the scalar `dead`; every later cell is left as it was.
+ */
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#define QSO_GROUP 32
+#define QSO_CHUNK 64
+
+/* ---- IEEE 754 binary16, written from the format's definition ---------------- */
+
+double qso_half_to_double(uint16_t h)
+{
+    int sign = h >> 15;
+    int e = (h >> 10) & 0x1f;
+    int f = h & 0x3ff;
+    double v;
+    if (e == 0)
+        v = ldexp((double)f, -24);                 /* zero or subnormal: f * 2^-24 */
+    else if (e == 31)
+        v = f ? NAN : INFINITY;
+    else
+        v = ldexp((double)(f | 0x400), e - 25);    /* (1024 + f) * 2^(e - 15 - 10) */
+    return sign ? -v : v;
+}
+
+/* Round a double to the nearest binary16, ties to even. */
+uint16_t qso_double_to_half(double x)
+{
+    uint16_t sign = signbit(x) ? 0x8000 : 0;
+    double a = fabs(x);
+    if (isnan(x))
+        return 0x7e00;
+    if (a >= 65520.0)                      /* halfway between 65504 and 2^16 rounds up */
+        return sign | 0x7c00;
+    if (a < ldexp(1.0, -14)) {             /* subnormal range: multiples of 2^-24 */
+        double r = rint(ldexp(a, 24));     /* exact scaling, then ties-to-even */
+        return sign | (uint16_t)r;         /* r == 1024 is the smallest normal */
+    }
+    int E;
+    frexp(a, &E);                          /* a = f * 2^E, f in [0.5, 1) */
+    int e = E - 1;                         /* a in [2^e, 2^(e+1)) */
+    double r = rint(ldexp(a, 10 - e));     /* significand in [1024, 2048] */
+    if (r == 2048.0) {
+        r = 1024.0;
+        e += 1;
+    }
+    if (e + 15 >= 31)
+        return sign | 0x7c00;
+    return sign | (uint16_t)(((e + 15) << 10) | ((int)r - 1024));
+}
+
+/* ---- attention ---------------------------------------------------------------- */
+
+static int32_t slot_id(const int32_t *ids, int64_t ids_stride, int32_t t, int32_t p, int64_t slot)
+{
+    if (ids)
+        return ids[(int64_t)t * ids_stride + slot];
+    return slot <= p ? (int32_t)slot : -1;     /* implicit row: every causal cell */
+}
+
+static double deq(const int8_t *x, const uint16_t *sc, int32_t D, int64_t c, int32_t d)
+{
+    int32_t G = D / QSO_GROUP;
+    return (double)x[c * D + d] * qso_half_to_double(sc[c * G + d / QSO_GROUP]);
+}
+
+/*
+ * Chunk records for tokens [t_begin, t_end).
+ * m, l : [T][C][H]; o : [T][C][H][D]   (all fp64, indexed by absolute t)
+ * oabs : optional [T][C][H][D], sum_j p_j |v_{c_j,d}| (magnitude used to bound
+ *        rounding error in tests), NULL to skip.
+ * C = ids_stride / 64, or ceil((pos0 + T) / 64) when ids == NULL.
+ * Returns 0, or -1 on a shape it does not handle.
+ */
+int qso_attn_chunks(const uint16_t *q, const int8_t *kq, const int8_t *vq,
+                    const uint16_t *ksc, const uint16_t *vsc, int32_t n_cells,
+                    const int32_t *ids, int32_t ids_stride,
+                    int32_t pos0, int32_t T, int32_t H, int32_t D, double scale,
+                    int32_t t_begin, int32_t t_end,
+                    double *m, double *l, double *o, double *oabs)
+{
+    if (D % QSO_GROUP != 0 || H < 1 || T < 0)
+        return -1;
+    int32_t C = ids ? ids_stride / QSO_CHUNK : (pos0 + T + QSO_CHUNK - 1) / QSO_CHUNK;
+    double S[QSO_CHUNK];
+    int32_t cell[QSO_CHUNK];
+    for (int32_t t = t_begin; t < t_end; ++t) {
+        int32_t p = pos0 + t;
+        for (int32_t k = 0; k < C; ++k) {
+            int n = 0;
+            for (int32_t s = 0; s < QSO_CHUNK; ++s) {
+                int32_t id = slot_id(ids, ids_stride, t, p, (int64_t)k * QSO_CHUNK + s);
+                if (id >= 0 && id < n_cells)
+                    cell[n++] = id;
+            }
+            for (int32_t h = 0; h < H; ++h) {
+                int64_t r = ((int64_t)t * C + k) * H + h;
+                if (n == 0) {
+                    m[r] = -INFINITY;
+                    l[r] = 0.0;
+                    continue;
+                }
+                const uint16_t *qr = q + ((int64_t)t * H + h) * D;
+                double mx = -INFINITY;
+                for (int j = 0; j < n; ++j) {
+                    double acc = 0.0;
+                    for (int32_t d = 0; d < D; ++d)
+                        acc += qso_half_to_double(qr[d]) * deq(kq, ksc, D, cell[j], d);
+                    S[j] = scale * acc;
+                    if (S[j] > mx)
+                        mx = S[j];
+                }
+                double sum = 0.0;
+                double *orow = o + r * D;
+                double *arow = oabs ? oabs + r * D : NULL;
+                for (int32_t d = 0; d < D; ++d) {
+                    orow[d] = 0.0;
+                    if (arow)
+                        arow[d] = 0.0;
+                }
+                for (int j = 0; j < n; ++j) {
+                    double pj = exp(S[j] - mx);
+                    sum += pj;
+                    for (int32_t d = 0; d < D; ++d) {
+                        double v = deq(vq, vsc, D, cell[j], d);
+                        orow[d] += pj * v;
+                        if (arow)
+                            arow[d] += pj * fabs(v);
+                    }
+                }
+                m[r] = mx;
+                l[r] = sum;
+            }
+        }
+    }
+    return 0;
+}
+
+/*
+ * Max-first merge of chunk records for tokens [t_begin, t_end).
+ * out64 : [T][H][D] fp64 value before rounding (may be NULL)
+ * out16 : [T][H][D] binary16 bits, round-to-nearest-even (may be NULL)
+ */
+int qso_merge(const double *m, const double *l, const double *o,
+              int32_t C, int32_t T, int32_t H, int32_t D,
+              int32_t t_begin, int32_t t_end, double *out64, uint16_t *out16)
+{
+    if (C < 0 || T < 0 || H < 1 || D < 1)
+        return -1;
+    for (int32_t t = t_begin; t < t_end; ++t) {
+        for (int32_t h = 0; h < H; ++h) {
+            int64_t orow = ((int64_t)t * H + h) * D;
+            double M = -INFINITY;
+            for (int32_t k = 0; k < C; ++k) {
+                double mk = m[((int64_t)t * C + k) * H + h];
+                if (mk != -INFINITY && mk > M)
+                    M = mk;
+            }
+            for (int32_t d = 0; d < D; ++d) {
+                double val;
+                if (M == -INFINITY) {
+                    val = 0.0;                     /* no valid slot in the row */
+                } else {
+                    double L = 0.0, O = 0.0;
+                    for (int32_t k = 0; k < C; ++k) {
+                        int64_t r = ((int64_t)t * C + k) * H + h;
+                        if (m[r] == -INFINITY)
+                            continue;
+                        double w = exp(m[r] - M);
+                        L += w * l[r];
+                        O += w * o[r * D + d];
+                    }
+                    val = O / L;
+                }
+                if (out64)
+                    out64[orow + d] = val;
+                if (out16)
+                    out16[orow + d] = qso_double_to_half(val);
+            }
+        }
+    }
+    return 0;
+}
+
+/*
+ * Causal scores for rows [t_begin, t_end).
+ * q : [T][Hs][D] fp32, k : [n_cells][D] fp32,
+ * scores : [T][row_stride] fp64; cells the method leaves untouched keep their value.
+ */
+int qso_score(const float *q, const float *k, int32_t n_cells, int32_t pos0, int32_t T,
+              int32_t Hs, int32_t D, double scale, double dead,
+              double *scores, int64_t row_stride, int32_t t_begin, int32_t t_end)
+{
+    if (Hs < 1 || D < 1 || n_cells < pos0 + T || row_stride < pos0 + T)
+        return -1;
+    for (int32_t t = t_begin; t < t_end; ++t) {
+        int64_t p = (int64_t)pos0 + t;
+        double *row = scores + (int64_t)t * row_stride;
+        for (int64_t c = 0; c <= p; ++c) {
+            double acc = 0.0;
+            for (int32_t h = 0; h < Hs; ++h) {
+                const float *qr = q + ((int64_t)t * Hs + h) * D;
+                for (int32_t d = 0; d < D; ++d)
+                    acc += (double)qr[d] * (double)k[c * D + d];
+            }
+            row[c] = scale * acc;
+        }
+        int64_t tile_end = QSO_CHUNK * ((p + 1 + QSO_CHUNK - 1) / QSO_CHUNK);
+        if (tile_end > row_stride)
+            tile_end = row_stride;
+        for (int64_t c = p + 1; c < tile_end; ++c)
+            row[c] = dead;
+    }
+    return 0;
+}

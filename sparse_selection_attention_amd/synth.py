@@ -1,0 +1,283 @@
+"""Seeded synthetic inputs for the explicit-selection attention path.
+
+This module only draws inputs. It holds none of the attention arithmetic and is
+shared by the tests, the benchmark and the smoke check, so that the CPU oracle
+and the HIP kernels are fed the same bytes.
+
+Workloads follow the pages' descriptions of their test data:
+  * "round 11 track b: qsa attention and score", section "boundaries and
+    provenance": seed 5, random signed int8 caches, finite positive fp16
+    scales, fp16 queries, explicit ids that are evenly spaced unique causal
+    cells, deterministic random fp32 inputs for the score kernel;
+  * "round 5 track b: cached residual norms and fused mtp attention", section
+    "mtp attention": the decode window is 64 sink cells, 256 previous local
+    cells and the current cell (321 cells, six 64-cell chunks).
+
+Random numbers come from SplitMix64 (Steele, Lea and Flood, "Fast splittable
+pseudorandom number generators", OOPSLA 2014) in its counter form: the i-th
+draw of a stream with key K is mix(K + (i + 1) * GAMMA). One stream per
+(seed, layer, tensor) keeps every tensor independent of how many values other
+tensors drew.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import List, Optional
+
+import numpy as np
+
+GAMMA = 0x9E3779B97F4A7C15
+_M1 = 0xBF58476D1CE4E5B9
+_M2 = 0x94D049BB133111EB
+_MASK = (1 << 64) - 1
+
+# tensor ids used to key the streams
+TID_Q, TID_KQ, TID_VQ, TID_KSC, TID_VSC, TID_SCORE_Q, TID_SCORE_K, TID_EDGE = range(8)
+
+HEAD_DIM = 128
+GROUP = 32          # one fp16 scale per 32 consecutive dims of a cached row
+CHUNK = 64          # selected slots are processed in 64-cell chunks
+SCALE_1_SQRT_128 = np.float32(1.0 / math.sqrt(128.0))
+
+
+def _mix_int(z: int) -> int:
+    z &= _MASK
+    z = ((z ^ (z >> 30)) * _M1) & _MASK
+    z = ((z ^ (z >> 27)) * _M2) & _MASK
+    return z ^ (z >> 31)
+
+
+def _mix_arr(z: np.ndarray) -> np.ndarray:
+    z = (z ^ (z >> np.uint64(30))) * np.uint64(_M1)
+    z = (z ^ (z >> np.uint64(27))) * np.uint64(_M2)
+    return z ^ (z >> np.uint64(31))
+
+
+def stream_key(seed: int, layer: int, tensor: int) -> int:
+    return _mix_int(seed) ^ _mix_int(1000 * layer + tensor)
+
+
+def raw_u64(key: int, n: int) -> np.ndarray:
+    """First n outputs of the SplitMix64 stream with the given key."""
+    with np.errstate(over="ignore"):
+        i = np.arange(1, n + 1, dtype=np.uint64)
+        state = np.uint64(key) + i * np.uint64(GAMMA)
+        return _mix_arr(state)
+
+
+def uniform01(key: int, n: int) -> np.ndarray:
+    """Doubles in [0, 1) from the top 53 bits of each draw."""
+    return (raw_u64(key, n) >> np.uint64(11)).astype(np.float64) * (2.0 ** -53)
+
+
+def normal(key: int, n: int) -> np.ndarray:
+    """Standard normals by the Box-Muller transform on consecutive draw pairs."""
+    m = (n + 1) // 2
+    u = uniform01(key, 2 * m)
+    u1, u2 = u[0::2], u[1::2]
+    r = np.sqrt(-2.0 * np.log1p(-u1))       # 1 - u1 lies in (0, 1]
+    z = np.empty(2 * m, dtype=np.float64)
+    z[0::2] = r * np.cos(2.0 * math.pi * u2)
+    z[1::2] = r * np.sin(2.0 * math.pi * u2)
+    return z[:n]
+
+
+def int8_sym(key: int, n: int) -> np.ndarray:
+    """Integers uniform in [-127, 127] (-128 is never drawn)."""
+    return ((raw_u64(key, n) % np.uint64(255)).astype(np.int64) - 127).astype(np.int8)
+
+
+def f16_uniform(key: int, n: int, lo: float, hi: float) -> np.ndarray:
+    """fp16 values (round-to-nearest-even from fp64) of U[lo, hi]."""
+    return (lo + (hi - lo) * uniform01(key, n)).astype(np.float16)
+
+
+# ---------------------------------------------------------------------------
+# selections
+
+
+def causal_all_ids(pos0: int, T: int, stride: int) -> np.ndarray:
+    """Row t lists cells 0..pos0+t in order, then -1 up to `stride` slots."""
+    ids = np.full((T, stride), -1, dtype=np.int32)
+    for t in range(T):
+        p = pos0 + t
+        ids[t, : p + 1] = np.arange(p + 1, dtype=np.int32)
+    return ids
+
+
+def evenly_spaced_ids(pos0: int, T: int, K: int) -> np.ndarray:
+    """Up to K evenly spaced unique causal cells per row, padded with -1.
+
+    Row t (p = pos0 + t) holds every cell 0..p when p + 1 <= K, otherwise
+    floor(j * p / (K - 1)) for j = 0..K-1: ascending, unique (the step p/(K-1)
+    is at least 1), and containing the sink cell 0 and the current cell p.
+    The row is padded with -1 to a whole number of 64-cell chunks.
+    """
+    stride = CHUNK * ((K + CHUNK - 1) // CHUNK)
+    ids = np.full((T, stride), -1, dtype=np.int32)
+    j = np.arange(K, dtype=np.int64)
+    for t in range(T):
+        p = pos0 + t
+        if p + 1 <= K:
+            ids[t, : p + 1] = np.arange(p + 1, dtype=np.int32)
+        else:
+            ids[t, :K] = (j * p) // (K - 1)
+    return ids
+
+
+def mtp_window_ids(pos0: int, ntok: int, sink: int = 64, local: int = 256) -> np.ndarray:
+    """Decode window: sink cells, the previous `local` cells, then the current cell."""
+    width = sink + local + 1
+    stride = CHUNK * ((width + CHUNK - 1) // CHUNK)
+    ids = np.full((ntok, stride), -1, dtype=np.int32)
+    for t in range(ntok):
+        p = pos0 + t
+        if p - local < sink:
+            raise ValueError("window overlaps the sink cells: p=%d" % p)
+        row = np.concatenate([np.arange(sink), np.arange(p - local, p), [p]])
+        ids[t, :width] = row
+    return ids
+
+
+# ---------------------------------------------------------------------------
+# attention cases
+
+
+@dataclasses.dataclass
+class Layer:
+    q: np.ndarray      # fp16 [T][H][D]
+    kq: np.ndarray     # int8 [n_cells][D]
+    vq: np.ndarray     # int8 [n_cells][D]
+    ksc: np.ndarray    # fp16 [n_cells][D/32]
+    vsc: np.ndarray    # fp16 [n_cells][D/32]
+
+
+@dataclasses.dataclass
+class AttnCase:
+    name: str
+    T: int
+    pos0: int
+    H: int
+    D: int
+    n_cells: int
+    ids: Optional[np.ndarray]   # int32 [T][ids_stride], or None for implicit all-causal rows
+    ids_stride: int
+    scale: np.float32
+    layers: List[Layer]
+
+    @property
+    def n_chunks(self) -> int:
+        if self.ids is None:
+            return (self.pos0 + self.T + CHUNK - 1) // CHUNK
+        return self.ids_stride // CHUNK
+
+
+def make_layer(seed: int, layer: int, T: int, H: int, n_cells: int, D: int = HEAD_DIM,
+               scale_lo: float = 1e-3, scale_hi: float = 2e-2) -> Layer:
+    G = D // GROUP
+    q = normal(stream_key(seed, layer, TID_Q), T * H * D).astype(np.float16).reshape(T, H, D)
+    kq = int8_sym(stream_key(seed, layer, TID_KQ), n_cells * D).reshape(n_cells, D)
+    vq = int8_sym(stream_key(seed, layer, TID_VQ), n_cells * D).reshape(n_cells, D)
+    ksc = f16_uniform(stream_key(seed, layer, TID_KSC), n_cells * G, scale_lo, scale_hi).reshape(n_cells, G)
+    vsc = f16_uniform(stream_key(seed, layer, TID_VSC), n_cells * G, scale_lo, scale_hi).reshape(n_cells, G)
+    return Layer(q, kq, vq, ksc, vsc)
+
+
+def make_case(name: str, T: int, pos0: int, H: int, ids: Optional[np.ndarray], layers: int = 1,
+              seed: int = 5, n_cells: Optional[int] = None, D: int = HEAD_DIM,
+              scale: np.float32 = SCALE_1_SQRT_128) -> AttnCase:
+    if n_cells is None:
+        n_cells = pos0 + T
+    stride = 0 if ids is None else int(ids.shape[1])
+    ls = [make_layer(seed, li, T, H, n_cells, D) for li in range(layers)]
+    return AttnCase(name, T, pos0, H, D, n_cells, ids, stride, np.float32(scale), ls)
+
+
+def tiny() -> AttnCase:
+    """T=16 at pos0=0, 2 heads, 16 cells, every causal cell selected, one chunk."""
+    return make_case("tiny", 16, 0, 2, causal_all_ids(0, 16, CHUNK))
+
+
+def mtp(ntok: int, layers: int = 1) -> AttnCase:
+    """Decode window at pos0=3000: 64 sink + 256 local + 1 current cells, 12 heads."""
+    return make_case("mtp%d" % ntok, ntok, 3000, 12, mtp_window_ids(3000, ntok), layers=layers)
+
+
+def prompt_start(implicit: bool = False, layers: int = 1, T: int = 1984) -> AttnCase:
+    """T=1984 at pos0=0, every causal cell selected (explicit ids, or implicit rows)."""
+    stride = CHUNK * ((T + CHUNK - 1) // CHUNK)
+    ids = None if implicit else causal_all_ids(0, T, stride)
+    return make_case("prompt" + ("_implicit" if implicit else ""), T, 0, 12, ids, layers=layers)
+
+
+def mid(layers: int = 3, T: int = 1984) -> AttnCase:
+    """T=1984 at pos0=8192, up to 2048 evenly spaced causal cells per row."""
+    return make_case("mid", T, 8192, 12, evenly_spaced_ids(8192, T, 2048), layers=layers)
+
+
+def long_ctx(layers: int = 3, T: int = 1984, variant: Optional[str] = None) -> AttnCase:
+    """T=1984 at pos0=30000, up to 2051 evenly spaced causal cells per row.
+
+    variant "signed_zero": for tokens t = 0 mod 4, heads 0 and 6 get q = -0.0 in
+    every dim, and cached K rows of cells c = 0 mod 3 are made non-negative, so
+    those scores are exactly -0 or +0.
+    variant "cancel": for tokens t = 1 mod 4, in each 32-dim group the first 16
+    dims of q are +-2^-24 (random signs) and the last 16 are their negatives, and
+    every cached K row repeats its first 16 dims of each group in the last 16, so
+    each group's dot product cancels to zero exactly.
+    """
+    name = "long" if variant is None else "long_" + variant
+    case = make_case(name, T, 30000, 12, evenly_spaced_ids(30000, T, 2051), layers=layers)
+    if variant is None:
+        return case
+    for li, L in enumerate(case.layers):
+        if variant == "signed_zero":
+            qb = L.q.view(np.uint16)
+            qb[0::4, [0, 6], :] = 0x8000
+            L.kq[0::3] = np.abs(L.kq[0::3])
+        elif variant == "cancel":
+            sign = raw_u64(stream_key(5, li, TID_EDGE), T * L.q.shape[1] * 4 * 16) & np.uint64(1)
+            sign = sign.reshape(T, L.q.shape[1], 4, 16)
+            qb = L.q.view(np.uint16).reshape(T, L.q.shape[1], 4, 32)
+            pos = np.where(sign == 0, 0x0001, 0x8001).astype(np.uint16)
+            neg = pos ^ np.uint16(0x8000)
+            qb[1::4, :, :, :16] = pos[1::4]
+            qb[1::4, :, :, 16:] = neg[1::4]
+            kq = L.kq.reshape(-1, 4, 32)
+            kq[:, :, 16:] = kq[:, :, :16]
+        else:
+            raise ValueError(variant)
+    return case
+
+
+# ---------------------------------------------------------------------------
+# score inputs
+
+
+@dataclasses.dataclass
+class ScoreCase:
+    name: str
+    T: int
+    pos0: int
+    Hs: int
+    D: int
+    n_cells: int
+    q: np.ndarray       # fp32 [T][Hs][D]
+    k: np.ndarray       # fp32 [n_cells][D]
+    scale: np.float32
+    dead: np.float32
+    row_stride: int
+
+
+def score_case(T: int = 1984, pos0: int = 0, Hs: int = 1, seed: int = 5, D: int = HEAD_DIM,
+               row_stride: Optional[int] = None, scale: float = 1.0,
+               dead: float = -math.inf, n_cells: Optional[int] = None) -> ScoreCase:
+    if n_cells is None:
+        n_cells = pos0 + T
+    if row_stride is None:
+        row_stride = pos0 + T
+    q = normal(stream_key(seed, 0, TID_SCORE_Q), T * Hs * D).astype(np.float32).reshape(T, Hs, D)
+    k = normal(stream_key(seed, 0, TID_SCORE_K), n_cells * D).astype(np.float32).reshape(n_cells, D)
+    return ScoreCase("score_T%d_p%d_h%d" % (T, pos0, Hs), T, pos0, Hs, D, n_cells, q, k,
+                     np.float32(scale), np.float32(dead), row_stride)
