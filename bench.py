@@ -1,0 +1,260 @@
+#!/usr/bin/env python3
+"""Benchmark of the explicit-selection attention path on one MI355X.
+
+Workload: long-context prompt attention -- T=1984 query tokens at pos0=30000,
+12 fp16 query heads over one int8 K/V head (head dim 128, per-32 fp16 scales),
+up to 2051 evenly spaced causal cells per token in 33 chunks, 3 independent
+layers, seed 5. One step is qsa_attn + qsa_merge for each of the 3 layers on
+one stream, with every input resident in HBM before the timed region.
+
+Prints one JSON line: query-token*heads per second, achieved algorithmic GB/s,
+the roofline of the dominant kernel (qsa_attn) measured with HIP events inside
+the timed region, the companion causal-score kernel, and the CPU oracle timed
+on a bounded sample on this host's cores.
+"""
+from __future__ import annotations
+
+import argparse
+import concurrent.futures as cf
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+FP32_MFMA_PEAK_TFLOPS = 157.3
+
+
+def attn_bytes(ids, n_cells, T, H, D, C):
+    """Algorithmic bytes of one qsa_attn launch, summed over tokens.
+
+    Per token: K+V rows and their scales once per valid cell (not per head),
+    every id slot, the token's q, and one (m, l) pair per chunk plus o[D] per
+    non-empty chunk for every head.
+    """
+    import numpy as np
+    v = (ids >= 0) & (ids < n_cells)
+    n = v.sum(axis=1)
+    c = v.reshape(T, C, 64).any(axis=2).sum(axis=1)
+    per = n * (2 * D + 2 * 2 * (D // 32)) + 4 * 64 * C + 2 * H * D + H * (8 * C + 4 * D * c)
+    return int(per.sum()), c
+
+
+def merge_bytes(T, H, D, C, c):
+    # reads (m, l) of every chunk and o of non-empty chunks, writes fp16 out
+    return int((H * 8 * C + H * 4 * D * c + 2 * H * D).sum()) if hasattr(c, "sum") else None
+
+
+def src_hash(path):
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()
+
+
+def read_traffic(profile_md, kernel_src):
+    """HBM bytes per launch from a committed counter summary, if it matches the source."""
+    try:
+        text = open(profile_md).read()
+    except OSError:
+        return None
+    m_hash = re.search(r"kernel source sha256:\s*([0-9a-f]{64})", text)
+    m_bytes = re.search(r"hbm bytes per launch:\s*([0-9]+)", text)
+    if not m_hash or not m_bytes or m_hash.group(1) != src_hash(kernel_src):
+        return None
+    return int(m_bytes.group(1))
+
+
+def cpu_baseline(case, out_gpu, n_tokens, threads):
+    """The oracle, as it stands, on a sample of layer-0 tokens, spread over host cores."""
+    import numpy as np
+    import oracle
+
+    L = case.layers[0]
+    toks = np.linspace(0, case.T - 1, n_tokens).astype(int).tolist()
+
+    def one(t):
+        m, l, o = oracle.attn_chunks(L.q[t: t + 1], L.kq, L.vq, L.ksc, L.vsc, case.ids[t: t + 1],
+                                     case.pos0 + t, case.scale)
+        return oracle.merge(m, l, o)[0][0]
+
+    t0 = time.perf_counter()
+    with cf.ThreadPoolExecutor(threads) as ex:
+        res = list(ex.map(one, toks))
+    dt = time.perf_counter() - t0
+    err = max(float(np.abs(out_gpu[t].astype(np.float64) - r).max()) for t, r in zip(toks, res))
+    return {
+        "value": n_tokens * case.H / dt,
+        "unit": "query-token*heads/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": "%d evenly spaced tokens of layer 0 of the same workload (fp64 C oracle, %d threads, %.1f s wall)"
+                  % (n_tokens, threads, dt),
+        "max_abs_diff_vs_gpu": err,
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--layers", type=int, default=3)
+    ap.add_argument("--cpu-tokens", type=int, default=96)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
+    ap.add_argument("--no-score", action="store_true", help="skip the companion score kernel")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="also run one device copy of this many MiB (for counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print("bench.py: this build runs on one GPU; --gpus %d is not supported (the path would shard by "
+              "query token, with no exchange between GPUs)" % args.gpus, file=sys.stderr)
+        return 2
+    if int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py: run one process on one GPU", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import sparse_selection_attention_amd as qsa
+    from sparse_selection_attention_amd import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    print("bench: generating inputs", file=sys.stderr, flush=True)
+    case = synth.long_ctx(layers=args.layers)
+    T, H, D, C = case.T, case.H, case.D, case.n_chunks
+    up = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    layers = [tuple(up(x) for x in (L.q, L.kq, L.vq, L.ksc, L.vsc)) for L in case.layers]
+    ids = up(case.ids)
+    part = qsa.alloc_part(T, H, D, C, device=dev)
+    outs = [torch.empty(T, H, D, dtype=torch.float16, device=dev) for _ in range(args.layers)]
+    stream = torch.cuda.current_stream()
+    scale = float(case.scale)
+
+    a_bytes, c_nonempty = attn_bytes(case.ids, case.n_cells, T, H, D, C)
+    m_bytes = merge_bytes(T, H, D, C, c_nonempty)
+
+    def step(ev=None):
+        for li, (q, kq, vq, ksc, vsc) in enumerate(layers):
+            if ev is not None:
+                ev[li][0].record(stream)
+            qsa.qsa_attn(q, kq, vq, ksc, vsc, ids, case.pos0, scale, part, stream=stream)
+            if ev is not None:
+                ev[li][1].record(stream)
+            qsa.qsa_merge(part, C, outs[li], stream=stream)
+            if ev is not None:
+                ev[li][2].record(stream)
+
+    print("bench: warmup", file=sys.stderr, flush=True)
+    for _ in range(max(1, args.warmup)):
+        step()
+    torch.cuda.synchronize()
+
+    print("bench: timing %d steps" % args.steps, file=sys.stderr, flush=True)
+    evs = [[[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.layers)]
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step(evs[s])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    attn_ms = [evs[s][li][0].elapsed_time(evs[s][li][1]) for s in range(args.steps) for li in range(args.layers)]
+    merge_ms = [evs[s][li][1].elapsed_time(evs[s][li][2]) for s in range(args.steps) for li in range(args.layers)]
+    step_ms = [evs[s][0][0].elapsed_time(evs[s][-1][2]) for s in range(args.steps)]
+    ms_per_step = wall * 1e3 / args.steps
+
+    attn_avg_s = float(np.mean(attn_ms)) * 1e-3
+    merge_avg_s = float(np.mean(merge_ms)) * 1e-3
+    attn_gbs = a_bytes / attn_avg_s / 1e9
+    step_bytes = args.layers * (a_bytes + m_bytes)
+    traffic = read_traffic(os.path.join(ROOT, "profiles", "qsa_attn_long_counters.md"),
+                           os.path.join(ROOT, "sparse_selection_attention_amd", "csrc", "qsa_attn.hip"))
+
+    result = {
+        "metric": "query-token*heads/sec + achieved HBM GB/s, T=1984 pos0=30000 attention",
+        "value": T * H * args.layers / (ms_per_step * 1e-3),
+        "unit": "query-token*heads/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic (seeded SplitMix64: fp16 N(0,1) queries, int8 uniform [-127,127] K/V, "
+                "fp16 U[1e-3,2e-2] scales)",
+        "config": {
+            "workload": "long-context prompt attention: T=1984, pos0=30000, 12 heads, head dim 128, one int8 K/V "
+                        "head with per-32 fp16 scales, 2051 evenly spaced causal cells in 33 chunks, %d layers"
+                        % args.layers,
+            "T": T, "pos0": case.pos0, "heads": H, "head_dim": D, "chunks": C, "selected": 2051,
+            "layers": args.layers, "n_cells": case.n_cells,
+        },
+        "achieved_gbs": step_bytes / (ms_per_step * 1e-3) / 1e9,
+        "algorithmic_bytes_per_step": step_bytes,
+        "step_ms_events_median": float(np.median(step_ms)),
+        "kernels": {
+            "qsa_attn": {"avg_us": attn_avg_s * 1e6, "bytes_per_launch": a_bytes, "gbs": attn_gbs},
+            "qsa_merge": {"avg_us": merge_avg_s * 1e6, "bytes_per_launch": m_bytes,
+                          "gbs": m_bytes / merge_avg_s / 1e9},
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": attn_gbs,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": attn_gbs / HBM_PEAK_GBS,
+            "traffic": traffic,
+        },
+    }
+
+    if not args.no_score:
+        sc = synth.score_case(T=T, pos0=case.pos0, Hs=12)
+        sq, sk = up(sc.q), up(sc.k)
+        scores = torch.empty(T, sc.row_stride, dtype=torch.float32, device=dev)
+        for _ in range(2):
+            qsa.qsa_score(sq, sk, sc.pos0, 1.0, float("-inf"), scores, stream=stream)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = 10
+        e0.record(stream)
+        for _ in range(reps):
+            qsa.qsa_score(sq, sk, sc.pos0, 1.0, float("-inf"), scores, stream=stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / reps
+        flops = 2.0 * 128 * sum(case.pos0 + t + 1 for t in range(T))   # heads summed before the contraction
+        result["companion_score"] = {
+            "workload": "qsa_score T=1984 pos0=30000 Hs=12 fp32",
+            "avg_us": us,
+            "roofline": {"bound": "mfma", "achieved": flops / (us * 1e-6) / 1e12, "peak": FP32_MFMA_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": flops / (us * 1e-6) / 1e12 / FP32_MFMA_PEAK_TFLOPS},
+        }
+        del scores
+
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        a = torch.empty(n, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        torch.cuda.synchronize()
+        b.copy_(a)
+        torch.cuda.synchronize()
+        result["copy_calibration_bytes"] = n
+
+    if not args.no_cpu:
+        print("bench: cpu baseline", file=sys.stderr, flush=True)
+        threads = max(1, min(16, len(os.sched_getaffinity(0))))
+        result["cpu_baseline"] = cpu_baseline(case, outs[0].cpu().numpy(), args.cpu_tokens, threads)
+
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,147 @@
+/*
+ * qsa.h -- C ABI of libqsa.so: explicit-selection attention over an int8 K/V
+ * cache shared by all query heads, its max-first chunk merge, and causal q.K
+ * scores, on AMD Instinct MI355X (gfx950).
+ *
+ * Every pointer argument is a DEVICE pointer to memory the caller owns. The
+ * library allocates nothing, keeps no per-call state and is safe to call from
+ * several host threads. Each call validates its arguments on the host, enqueues
+ * its kernels on `stream` (a hipStream_t; NULL means the null stream) and
+ * returns without synchronising: inputs must stay alive, and outputs must not be
+ * read, until the stream has passed the call.
+ *
+ * Status codes:
+ *   QSA_OK              success (also for T == 0, which enqueues nothing)
+ *   QSA_ERR_ARG         a required pointer is NULL or misaligned, or a size is
+ *                       negative or inconsistent; nothing was enqueued
+ *   QSA_ERR_UNSUPPORTED a shape this build does not implement (D != 128, more
+ *                       than 16 heads, more than 2^25 cached rows) or a device
+ *                       that is not gfx950
+ *   QSA_ERR_DEVICE      a HIP runtime call failed (message in qsa_last_error)
+ *
+ * Names follow the pages' notation: q, kq/vq, ksc/vsc, ids with -1 poison,
+ * pos0, T and a softmax scale ("round 11 track b: qsa attention and score",
+ * section "boundaries and provenance").
+ */
+#ifndef QSA_H
+#define QSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    QSA_OK = 0,
+    QSA_ERR_ARG = 1,
+    QSA_ERR_UNSUPPORTED = 2,
+    QSA_ERR_DEVICE = 3
+} qsa_status;
+
+/* Symbols of the library; everything else in it is hidden. */
+#define QSA_API __attribute__((visibility("default")))
+
+/* Slots of an id row are processed in chunks of this many. */
+#define QSA_CHUNK 64
+/* Cached rows carry one fp16 scale per this many consecutive dims. */
+#define QSA_GROUP 32
+
+/*
+ * qsa_attn -- chunk records of explicit-selection attention.
+ *
+ * Defined by "round 11 track b: qsa attention and score", section
+ * "implementation and evaluator" (int8 K/V rows addressed by selected cell
+ * ids, four scale groups per row, incomplete 64-cell chunks, empty slots that
+ * contribute nothing, the partial buffer written before the merge), and by
+ * "round 5 track b: cached residual norms and fused mtp attention", section
+ * "mtp attention" (per-64-cell chunk arithmetic with per-chunk maxima and
+ * denominators, one V load per dim per cell for all heads).
+ *
+ * For each query token t (cache position p = pos0 + t), each chunk k of its id
+ * row (slots 64k .. 64k+63) and each head h < H, with the valid slots j of the
+ * chunk (0 <= id < n_cells):
+ *   k_d = kq[c][d] * ksc[c][d/32],  v_d = vq[c][d] * vsc[c][d/32]
+ *   S_j = scale * sum_d q[t][h][d] * k_d
+ *   m   = max_j S_j,  p_j = exp(S_j - m),  l = sum_j p_j,  o[d] = sum_j p_j v_d
+ * and writes the record (m, l, o) to `part`. A chunk with no valid slot gets
+ * m = -inf and l = +0, and its o is not written.
+ *
+ * q        fp16 [T][H][D], row-major, 16-byte aligned
+ * kq, vq   int8 [n_cells][D], 16-byte aligned rows; n_cells <= 2^25
+ * ksc, vsc fp16 [n_cells][D/32], finite and positive, 8-byte aligned
+ * ids      int32 [T][ids_stride], -1 = poison. Any id outside [0, n_cells) is
+ *          treated as poison and never dereferenced. ids_stride must be a
+ *          positive multiple of 64; the row has C = ids_stride / 64 chunks.
+ *          Selected ids are trusted to be causal (id <= p); duplicates count
+ *          once per occurrence.
+ *          ids == NULL selects implicit rows: slot j holds cell j when j <= p
+ *          (else poison), with C = ceil((pos0 + T) / 64); ids_stride is ignored.
+ * pos0     cache position of token 0 (>= 0); T query tokens (>= 0)
+ * H        query heads sharing the one K/V head, 1..16
+ * D        head dim; this build implements D == 128 only
+ * scale    softmax scale applied to every dot product
+ * part     qsa_part_bytes(T, H, D, C) bytes, 256-byte aligned; laid out as
+ *          o[T][C][H][D] fp32, then m[T][C][H] fp32, then l[T][C][H] fp32,
+ *          each sub-array starting on a 256-byte boundary
+ *          (qsa_part_offsets gives the byte offsets).
+ */
+QSA_API qsa_status qsa_attn(const void *q, const int8_t *kq, const int8_t *vq,
+                    const void *ksc, const void *vsc, int32_t n_cells,
+                    const int32_t *ids, int32_t ids_stride,
+                    int32_t pos0, int32_t T, int32_t H, int32_t D,
+                    float scale, void *part, void *stream);
+
+/*
+ * qsa_merge -- max-first merge of chunk records into fp16 output.
+ *
+ * Defined by "round 5 track b: cached residual norms and fused mtp attention",
+ * sections "preflight / ownership" and "mtp attention" (the max-first chunk
+ * merge). For each token t and head h, over chunks with m_k != -inf:
+ *   M = max_k m_k,  w_k = exp(m_k - M),  L = sum_k w_k l_k,
+ *   out[t][h][d] = fp16_rne( sum_k w_k o_k[d] / L )
+ * A (t, h) with no such chunk gets +0 in every dim. Records with m = -inf are
+ * skipped and their o is never read.
+ *
+ * part     records written by qsa_attn with the same T, H, D and n_chunks
+ * out      fp16 [T][H][D], 16-byte aligned
+ */
+QSA_API qsa_status qsa_merge(const void *part, int32_t n_chunks, int32_t T, int32_t H, int32_t D,
+                     void *out, void *stream);
+
+/*
+ * qsa_score -- fp32 q.K scores over causal cells with a dead-key tail.
+ *
+ * Defined by "round 11 track b: qsa attention and score", sections
+ * "implementation and evaluator" (scores over causal cells, a scalar dead-key
+ * tail, beyond-causal cells left untouched) and "score: valid negative result"
+ * (64-cell tiles, a head reduction). For row t (p = pos0 + t):
+ *   scores[t][c] = scale * sum_{h < Hs} sum_d q[t][h][d] * k[c][d]   for c <= p
+ *   scores[t][c] = dead       for p < c < min(64 * ceil((p + 1) / 64), row_stride)
+ * and every later cell of the row is left untouched.
+ *
+ * q        fp32 [T][Hs][D], 16-byte aligned;  Hs in 1..16
+ * k        fp32 [n_cells][D], 16-byte aligned; n_cells >= pos0 + T
+ * scores   fp32 [T][row_stride]; row_stride >= pos0 + T; 4-byte aligned
+ * D        this build implements D == 128 only
+ */
+QSA_API qsa_status qsa_score(const float *q, const float *k, int32_t n_cells, int32_t pos0,
+                     int32_t T, int32_t Hs, int32_t D, float scale, float dead,
+                     float *scores, int64_t row_stride, void *stream);
+
+/* Bytes of the `part` workspace for T tokens, H heads, head dim D, n_chunks chunks. */
+QSA_API size_t qsa_part_bytes(int32_t T, int32_t H, int32_t D, int32_t n_chunks);
+
+/* Byte offsets of the o, m and l sub-arrays inside `part` (any may be NULL). */
+QSA_API void qsa_part_offsets(int32_t T, int32_t H, int32_t D, int32_t n_chunks,
+                      size_t *o_off, size_t *m_off, size_t *l_off);
+
+/* Message for the last non-OK status returned on the calling thread ("" if none). */
+QSA_API const char *qsa_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QSA_H */

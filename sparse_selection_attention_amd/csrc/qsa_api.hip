@@ -1,0 +1,244 @@
+// qsa_api.hip -- the C ABI of libqsa.so (declared in include/qsa.h).
+//
+// Every entry point checks its arguments on the host before anything reaches
+// the device, so a bad call is rejected with QSA_ERR_ARG or
+// QSA_ERR_UNSUPPORTED and enqueues nothing. Kernels are enqueued on the
+// caller's stream and the call returns without synchronising.
+#include "qsa.h"
+#include "qsa_internal.h"
+
+#include <atomic>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+qsa_status fail(qsa_status st, const char *fmt, ...)
+{
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+qsa_status ok()
+{
+    g_err[0] = '\0';
+    return QSA_OK;
+}
+
+bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+// Per-device answer to "is this a gfx950?": 0 unknown, 1 yes, 2 no.
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_arch_ok[kMaxDevices];
+
+qsa_status check_device()
+{
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return fail(QSA_ERR_DEVICE, "hipGetDevice: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(QSA_ERR_UNSUPPORTED, "device index %d out of range", dev);
+    int st = g_arch_ok[dev].load(std::memory_order_relaxed);
+    if (st == 0) {
+        hipDeviceProp_t prop;
+        e = hipGetDeviceProperties(&prop, dev);
+        if (e != hipSuccess)
+            return fail(QSA_ERR_DEVICE, "hipGetDeviceProperties: %s", hipGetErrorString(e));
+        st = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+        g_arch_ok[dev].store(st, std::memory_order_relaxed);
+        if (st == 2)
+            return fail(QSA_ERR_UNSUPPORTED, "device %d is %s, this library is built for gfx950",
+                        dev, prop.gcnArchName);
+    }
+    if (st == 2)
+        return fail(QSA_ERR_UNSUPPORTED, "device %d is not a gfx950", dev);
+    return QSA_OK;
+}
+
+qsa_status launched(hipError_t e, const char *what)
+{
+    if (e != hipSuccess)
+        return fail(QSA_ERR_DEVICE, "%s launch: %s", what, hipGetErrorString(e));
+    return ok();
+}
+
+} // namespace
+
+extern "C" {
+
+size_t qsa_part_bytes(int32_t T, int32_t H, int32_t D, int32_t n_chunks)
+{
+    if (T < 0 || H < 0 || D < 0 || n_chunks < 0)
+        return 0;
+    size_t total = 0;
+    qsa::part_layout(T, H, D, n_chunks, nullptr, nullptr, nullptr, &total);
+    return total;
+}
+
+void qsa_part_offsets(int32_t T, int32_t H, int32_t D, int32_t n_chunks,
+                      size_t *o_off, size_t *m_off, size_t *l_off)
+{
+    if (T < 0 || H < 0 || D < 0 || n_chunks < 0) {
+        if (o_off) *o_off = 0;
+        if (m_off) *m_off = 0;
+        if (l_off) *l_off = 0;
+        return;
+    }
+    qsa::part_layout(T, H, D, n_chunks, o_off, m_off, l_off, nullptr);
+}
+
+const char *qsa_last_error(void) { return g_err; }
+
+qsa_status qsa_attn(const void *q, const int8_t *kq, const int8_t *vq,
+                    const void *ksc, const void *vsc, int32_t n_cells,
+                    const int32_t *ids, int32_t ids_stride,
+                    int32_t pos0, int32_t T, int32_t H, int32_t D,
+                    float scale, void *part, void *stream)
+{
+    if (T < 0 || pos0 < 0 || n_cells < 0)
+        return fail(QSA_ERR_ARG, "qsa_attn: negative T (%d), pos0 (%d) or n_cells (%d)", T, pos0, n_cells);
+    if (H < 1)
+        return fail(QSA_ERR_ARG, "qsa_attn: H must be >= 1 (got %d)", H);
+    if (H > qsa::kMaxHeads)
+        return fail(QSA_ERR_UNSUPPORTED, "qsa_attn: at most %d heads (got %d)", qsa::kMaxHeads, H);
+    if (D != qsa::kD)
+        return fail(QSA_ERR_UNSUPPORTED, "qsa_attn: head dim %d not implemented (only %d)", D, qsa::kD);
+    if (ids && (ids_stride <= 0 || ids_stride % QSA_CHUNK != 0))
+        return fail(QSA_ERR_ARG, "qsa_attn: ids_stride must be a positive multiple of %d (got %d)",
+                    QSA_CHUNK, ids_stride);
+    if ((int64_t)pos0 + T > INT32_MAX)
+        return fail(QSA_ERR_ARG, "qsa_attn: pos0 + T overflows int32");
+    if (n_cells > qsa::kMaxCells)
+        return fail(QSA_ERR_UNSUPPORTED, "qsa_attn: at most %d cached rows (got %d)", qsa::kMaxCells, n_cells);
+    if (T == 0)
+        return ok();
+    if (!q || !kq || !vq || !ksc || !vsc || !part)
+        return fail(QSA_ERR_ARG, "qsa_attn: NULL q, kq, vq, ksc, vsc or part");
+    if (!aligned(q, 16) || !aligned(kq, 16) || !aligned(vq, 16) || !aligned(ksc, 8) ||
+        !aligned(vsc, 8) || !aligned(part, 256) || (ids && !aligned(ids, 4)))
+        return fail(QSA_ERR_ARG, "qsa_attn: misaligned pointer (q, kq, vq: 16 B; ksc, vsc: 8 B; "
+                                 "part: 256 B; ids: 4 B)");
+    const int64_t C = ids ? ids_stride / QSA_CHUNK : ((int64_t)pos0 + T + QSA_CHUNK - 1) / QSA_CHUNK;
+    const int64_t n_items = (int64_t)T * C;
+    const int64_t n_blocks = (n_items + qsa::kAttnWaves - 1) / qsa::kAttnWaves;
+    const int64_t per_xcd = (n_blocks + 7) / 8;
+    if (C > INT32_MAX || per_xcd * 8 > INT32_MAX)
+        return fail(QSA_ERR_ARG, "qsa_attn: T * chunks too large for one launch");
+    qsa_status st = check_device();
+    if (st != QSA_OK)
+        return st;
+
+    size_t o_off, m_off, l_off;
+    qsa::part_layout(T, H, D, C, &o_off, &m_off, &l_off, nullptr);
+    char *pb = static_cast<char *>(part);
+    qsa::AttnArgs a;
+    a.q = static_cast<const _Float16 *>(q);
+    a.kq = kq;
+    a.vq = vq;
+    a.ksc = static_cast<const uint16_t *>(ksc);
+    a.vsc = static_cast<const uint16_t *>(vsc);
+    a.ids = ids;
+    a.ids_stride = ids ? ids_stride : 0;
+    a.n_cells = n_cells;
+    a.pos0 = pos0;
+    a.T = T;
+    a.H = H;
+    a.C = (int32_t)C;
+    a.scale = scale;
+    a.o = reinterpret_cast<float *>(pb + o_off);
+    a.m = reinterpret_cast<float *>(pb + m_off);
+    a.l = reinterpret_cast<float *>(pb + l_off);
+    a.n_items = n_items;
+    a.n_blocks = (int32_t)n_blocks;
+    a.blocks_per_xcd = (int32_t)per_xcd;
+    return launched(qsa::launch_attn(a, static_cast<hipStream_t>(stream)), "qsa_attn");
+}
+
+qsa_status qsa_merge(const void *part, int32_t n_chunks, int32_t T, int32_t H, int32_t D,
+                     void *out, void *stream)
+{
+    if (T < 0 || n_chunks < 0)
+        return fail(QSA_ERR_ARG, "qsa_merge: negative T (%d) or n_chunks (%d)", T, n_chunks);
+    if (H < 1)
+        return fail(QSA_ERR_ARG, "qsa_merge: H must be >= 1 (got %d)", H);
+    if (H > qsa::kMaxHeads)
+        return fail(QSA_ERR_UNSUPPORTED, "qsa_merge: at most %d heads (got %d)", qsa::kMaxHeads, H);
+    if (D != qsa::kD)
+        return fail(QSA_ERR_UNSUPPORTED, "qsa_merge: head dim %d not implemented (only %d)", D, qsa::kD);
+    if (T == 0)
+        return ok();
+    if (!part || !out)
+        return fail(QSA_ERR_ARG, "qsa_merge: NULL part or out");
+    if (!aligned(part, 256) || !aligned(out, 16))
+        return fail(QSA_ERR_ARG, "qsa_merge: misaligned pointer (part: 256 B; out: 16 B)");
+    if (((int64_t)T * H + 3) / 4 > INT32_MAX)
+        return fail(QSA_ERR_ARG, "qsa_merge: T * H too large for one launch");
+    qsa_status st = check_device();
+    if (st != QSA_OK)
+        return st;
+    size_t o_off, m_off, l_off;
+    qsa::part_layout(T, H, D, n_chunks, &o_off, &m_off, &l_off, nullptr);
+    const char *pb = static_cast<const char *>(part);
+    qsa::MergeArgs a;
+    a.o = reinterpret_cast<const float *>(pb + o_off);
+    a.m = reinterpret_cast<const float *>(pb + m_off);
+    a.l = reinterpret_cast<const float *>(pb + l_off);
+    a.C = n_chunks;
+    a.T = T;
+    a.H = H;
+    a.out = static_cast<_Float16 *>(out);
+    return launched(qsa::launch_merge(a, static_cast<hipStream_t>(stream)), "qsa_merge");
+}
+
+qsa_status qsa_score(const float *q, const float *k, int32_t n_cells, int32_t pos0,
+                     int32_t T, int32_t Hs, int32_t D, float scale, float dead,
+                     float *scores, int64_t row_stride, void *stream)
+{
+    if (T < 0 || pos0 < 0 || n_cells < 0)
+        return fail(QSA_ERR_ARG, "qsa_score: negative T (%d), pos0 (%d) or n_cells (%d)", T, pos0, n_cells);
+    if (Hs < 1)
+        return fail(QSA_ERR_ARG, "qsa_score: Hs must be >= 1 (got %d)", Hs);
+    if (Hs > qsa::kMaxHeads)
+        return fail(QSA_ERR_UNSUPPORTED, "qsa_score: at most %d heads (got %d)", qsa::kMaxHeads, Hs);
+    if (D != qsa::kD)
+        return fail(QSA_ERR_UNSUPPORTED, "qsa_score: head dim %d not implemented (only %d)", D, qsa::kD);
+    if ((int64_t)pos0 + T > INT32_MAX)
+        return fail(QSA_ERR_ARG, "qsa_score: pos0 + T overflows int32");
+    if ((int64_t)n_cells < (int64_t)pos0 + T)
+        return fail(QSA_ERR_ARG, "qsa_score: n_cells (%d) < pos0 + T (%lld)", n_cells, (long long)pos0 + T);
+    if (row_stride < (int64_t)pos0 + T)
+        return fail(QSA_ERR_ARG, "qsa_score: row_stride (%lld) < pos0 + T (%lld)", (long long)row_stride,
+                    (long long)pos0 + T);
+    if (((int64_t)T + 63) / 64 > 65535)
+        return fail(QSA_ERR_ARG, "qsa_score: T too large for one launch");
+    if (T == 0)
+        return ok();
+    if (!q || !k || !scores)
+        return fail(QSA_ERR_ARG, "qsa_score: NULL q, k or scores");
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(scores, 4))
+        return fail(QSA_ERR_ARG, "qsa_score: misaligned pointer (q, k: 16 B; scores: 4 B)");
+    qsa_status st = check_device();
+    if (st != QSA_OK)
+        return st;
+    qsa::ScoreArgs a;
+    a.q = q;
+    a.k = k;
+    a.n_cells = n_cells;
+    a.pos0 = pos0;
+    a.T = T;
+    a.Hs = Hs;
+    a.scale = scale;
+    a.dead = dead;
+    a.scores = scores;
+    a.row_stride = row_stride;
+    return launched(qsa::launch_score(a, static_cast<hipStream_t>(stream)), "qsa_score");
+}
+
+} // extern "C"

@@ -1,0 +1,334 @@
+// qsa_attn.hip -- chunk records of explicit-selection attention on gfx950.
+//
+// What is computed follows "round 11 track b: qsa attention and score",
+// section "implementation and evaluator" (int8 K/V rows gathered by selected
+// cell id, four scale groups per K row, incomplete 64-cell chunks, empty slots
+// that contribute nothing) and "round 5 track b: cached residual norms and
+// fused mtp attention", section "mtp attention" (per-chunk max, denominator and
+// partial output; one V load per dim per cell for all heads).
+//
+// Design on CDNA4. One 64-lane wave owns one (token, chunk) pair:
+//   * lane c reads slot c's id; a ballot gives the chunk's valid mask;
+//   * the 64 cells' K and V rows are read once for all heads: MFMA tiles put the
+//     heads (up to 16) on one tile dimension and the cells on the other;
+//   * QK: v_mfma_f32_16x16x32_f16 with A = K rows (16 cells x 32 dims of one
+//     scale group, int8 converted exactly to fp16) and B = q (32 dims x 16
+//     heads), giving one fp32 partial per scale group that is then weighted by
+//     the cell's group scale -- the four per-group partials of the pages;
+//   * the chunk max and denominator are lane-local folds plus two cross-row
+//     exchanges, because the score tile already holds one head per lane column;
+//   * PV: v_mfma_f32_16x16x32_f16 with A = p (heads x 32 cells) straight from
+//     the score tile's registers, and B = V rows dequantised to fp16. Both sides
+//     are split into fp16 high and low parts and contracted as
+//     hi*hi + hi*lo + lo*hi, so the products carry about 22 bits:
+//       - vq * vsc has at most 18 significant bits, so V = V_hi + V_lo exactly,
+//         with V_lo formed by one fp16 fma; the V scales of the chunk are first
+//         multiplied by a common power of two so the largest lies in [1, 2),
+//         which keeps vq * vsc inside fp16 range, and that exact power of two is
+//         taken back out of the fp32 result;
+//       - p = P_hi + P_lo to within 2^-22 relative;
+//     a single fp16 rounding of p and of v would cost up to 2^-12 |v| per
+//     term, which is too coarse when a chunk holds a few cells whose values
+//     nearly cancel;
+//   * int8 bytes become fp16 with one SDWA conversion each, the byte picked
+//     straight out of the loaded dword.
+// Work items are ordered chunk-major (all tokens of chunk 0, then chunk 1, ...)
+// and each XCD walks a contiguous range of them, so the cells one XCD gathers
+// stay within a narrow band of the cache and are served from its own L2.
+#include "qsa_internal.h"
+
+namespace qsa {
+namespace {
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWaves = kAttnWaves;         // waves (work items) per workgroup
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ inline float half_bits_to_float(uint32_t bits16)
+{
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)bits16);
+}
+
+__device__ inline uint32_t wave_max_u32(uint32_t x)
+{
+#pragma unroll
+    for (int s = 32; s >= 1; s >>= 1)
+        x = max(x, (uint32_t)__shfl_xor((int)x, s, 64));
+    return x;
+}
+
+// int8 -> fp16 (exact) with SDWA: byte BA of x into the low half, byte BB of y
+// into the high half of one dword.
+#define QSA_CVT2(out, x, ba, y, bb)                                                              \
+    asm("v_cvt_f16_i16_sdwa %0, sext(%1) dst_sel:WORD_0 dst_unused:UNUSED_PAD src0_sel:BYTE_" #ba  \
+        "\n\tv_cvt_f16_i16_sdwa %0, sext(%2) dst_sel:WORD_1 dst_unused:UNUSED_PRESERVE "          \
+        "src0_sel:BYTE_" #bb                                                                      \
+        : "=&v"(out)                                                                             \
+        : "v"(x), "v"(y))
+
+template <int B>
+__device__ inline uint32_t cvt2_byte(uint32_t x, uint32_t y)
+{
+    uint32_t r;
+    if constexpr (B == 0)
+        QSA_CVT2(r, x, 0, y, 0);
+    else if constexpr (B == 1)
+        QSA_CVT2(r, x, 1, y, 1);
+    else if constexpr (B == 2)
+        QSA_CVT2(r, x, 2, y, 2);
+    else
+        QSA_CVT2(r, x, 3, y, 3);
+    return r;
+}
+
+// Same with a byte index that is a constant once the caller's loop is unrolled.
+__device__ inline uint32_t cvt2_sel(int b, uint32_t x, uint32_t y)
+{
+    switch (b) {
+    case 0: return cvt2_byte<0>(x, y);
+    case 1: return cvt2_byte<1>(x, y);
+    case 2: return cvt2_byte<2>(x, y);
+    default: return cvt2_byte<3>(x, y);
+    }
+}
+
+// Eight int8 values (little-endian in v) to fp16, exactly, in byte order.
+__device__ inline half8 i8x8_to_half8(uint2 v)
+{
+    uint32_t a, b, c, d;
+    QSA_CVT2(a, v.x, 0, v.x, 1);
+    QSA_CVT2(b, v.x, 2, v.x, 3);
+    QSA_CVT2(c, v.y, 0, v.y, 1);
+    QSA_CVT2(d, v.y, 2, v.y, 3);
+    uint4 u = make_uint4(a, b, c, d);
+    return __builtin_bit_cast(half8, u);
+}
+
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+
+__device__ inline void wave_sync_lds()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+__global__ __launch_bounds__(64 * kWaves) void attn_kernel(AttnArgs a)
+{
+    __shared__ float4 s_ksc[kWaves][kChunk];        // scale * ksc of each cell, fp32
+    __shared__ uint16_t s_vsc[kWaves][4][kChunk];   // group-major, so adjacent cells pair up
+    __shared__ int32_t s_id[kWaves][kChunk];
+
+    const int lane = threadIdx.x & 63;
+    const int w = threadIdx.x >> 6;
+    const int j = lane >> 4;        // 16-lane row of the wave
+    const int c16 = lane & 15;      // column inside a 16-wide MFMA tile
+
+    // each XCD (workgroup id mod 8) walks a contiguous range of workgroups
+    const int lb = (blockIdx.x & 7) * a.blocks_per_xcd + (blockIdx.x >> 3);
+    if (lb >= a.n_blocks)
+        return;
+    const int64_t item = (int64_t)lb * kWaves + w;
+    if (item >= a.n_items)
+        return;
+    const int k = (int)(item / a.T);
+    const int t = (int)(item - (int64_t)k * a.T);
+    const int p = a.pos0 + t;
+
+    // ---- ids and the valid mask --------------------------------------------
+    const int64_t slot = (int64_t)k * kChunk + lane;
+    int32_t id;
+    if (a.ids)
+        id = a.ids[(int64_t)t * a.ids_stride + slot];
+    else
+        id = slot <= p ? (int32_t)slot : -1;
+    const bool valid = (uint32_t)id < (uint32_t)a.n_cells;
+    const int32_t sid = valid ? id : 0;
+    const uint64_t mask = __ballot(valid);
+
+    const int64_t rec = ((int64_t)t * a.C + k) * a.H;
+    if (mask == 0) {                // empty chunk: (-inf, +0), o left alone
+        if (lane < a.H) {
+            a.m[rec + lane] = -INFINITY;
+            a.l[rec + lane] = 0.0f;
+        }
+        return;
+    }
+
+    // ---- per-cell scales (zero for empty slots); K scales carry the softmax scale
+    uint2 ks = make_uint2(0u, 0u), vs = make_uint2(0u, 0u);
+    if (valid) {
+        ks = *(const uint2 *)(a.ksc + (int64_t)sid * 4);
+        vs = *(const uint2 *)(a.vsc + (int64_t)sid * 4);
+    }
+    // largest biased fp16 exponent among the chunk's V scales
+    uint32_t e = max(max((vs.x >> 10) & 31u, (vs.x >> 26) & 31u),
+                     max((vs.y >> 10) & 31u, (vs.y >> 26) & 31u));
+    e = wave_max_u32(e);
+    const float up = __int_as_float((127 + 15 - (int)e) << 23);     // 2^(15 - e)
+    const float down = __int_as_float((127 - 15 + (int)e) << 23);   // 2^(e - 15)
+    uint2 vn;
+    {
+        _Float16 h0 = (_Float16)(half_bits_to_float(vs.x & 0xffffu) * up);
+        _Float16 h1 = (_Float16)(half_bits_to_float(vs.x >> 16) * up);
+        _Float16 h2 = (_Float16)(half_bits_to_float(vs.y & 0xffffu) * up);
+        _Float16 h3 = (_Float16)(half_bits_to_float(vs.y >> 16) * up);
+        vn.x = (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
+        vn.y = (uint32_t)__builtin_bit_cast(uint16_t, h2) | ((uint32_t)__builtin_bit_cast(uint16_t, h3) << 16);
+    }
+    s_ksc[w][lane] = make_float4(a.scale * half_bits_to_float(ks.x & 0xffffu), a.scale * half_bits_to_float(ks.x >> 16),
+                                 a.scale * half_bits_to_float(ks.y & 0xffffu), a.scale * half_bits_to_float(ks.y >> 16));
+    s_vsc[w][0][lane] = (uint16_t)(vn.x & 0xffffu);
+    s_vsc[w][1][lane] = (uint16_t)(vn.x >> 16);
+    s_vsc[w][2][lane] = (uint16_t)(vn.y & 0xffffu);
+    s_vsc[w][3][lane] = (uint16_t)(vn.y >> 16);
+    s_id[w][lane] = sid;
+    wave_sync_lds();
+
+    // ---- gathers: K rows (A operand of QK), V rows (B operand of PV), q -----
+    // K: lane (j, c16) of block b holds cell 16b + c16, dims 32g + 8j .. +7.
+    uint2 kraw[4][4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+        const uint32_t kr = (uint32_t)s_id[w][16 * b + c16] * kD + 8 * j;   // n_cells * 128 < 2^32
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+            kraw[b][g] = *(const uint2 *)(a.kq + (kr + 32 * g));
+    }
+    // V: slot s of k-step ks is cell 32ks + 16(s/4) + 4j + s%4 -- the cells whose
+    // scores this lane holds -- and the lane reads dims 8*c16 .. 8*c16+7.
+    uint2 vraw[2][8];
+#pragma unroll
+    for (int ks2 = 0; ks2 < 2; ++ks2)
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+            const int cell = 32 * ks2 + 16 * (s >> 2) + 4 * j + (s & 3);
+            vraw[ks2][s] = *(const uint2 *)(a.vq + ((uint32_t)s_id[w][cell] * kD + 8 * c16));
+        }
+    // q: head c16, dims 32g + 8j .. +7 (zero for padding heads)
+    half8 qop[4];
+    if (c16 < a.H) {
+        const half8 *qr = (const half8 *)(a.q + ((int64_t)t * a.H + c16) * kD + 8 * j);
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+            qop[g] = qr[4 * g];
+    } else {
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+            qop[g] = (half8)(_Float16)0.0f;
+    }
+
+    // ---- scores: S[b][r] is cell 16b + 4j + r, head c16 ----------------------
+    float S[4][4];
+    const floatx4 zero = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+        floatx4 acc[4];
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+            acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(i8x8_to_half8(kraw[b][g]), qop[g], zero, 0, 0, 0);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int cell = 16 * b + 4 * j + r;
+            const float4 kb = s_ksc[w][cell];
+            const float sv = (acc[0][r] * kb.x + acc[1][r] * kb.y) + (acc[2][r] * kb.z + acc[3][r] * kb.w);
+            S[b][r] = ((mask >> cell) & 1ull) ? sv : -INFINITY;
+        }
+    }
+
+    // ---- chunk max and denominator per head ----------------------------------
+    float mx = -INFINITY;
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            mx = fmaxf(mx, S[b][r]);
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+
+    float P[4][4];
+    float lsum = 0.0f;
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            P[b][r] = __builtin_amdgcn_exp2f((S[b][r] - mx) * kLog2e);   // exp(0) = 1 exactly
+            lsum += P[b][r];
+        }
+    lsum += __shfl_xor(lsum, 16, 64);
+    lsum += __shfl_xor(lsum, 32, 64);
+
+    // ---- PV: O[tt] is heads 4j + r, dim 8*c16 + tt ---------------------------
+    floatx4 O[8];
+#pragma unroll
+    for (int tt = 0; tt < 8; ++tt)
+        O[tt] = zero;
+#pragma unroll
+    for (int ks2 = 0; ks2 < 2; ++ks2) {
+        // A operand: p of slots s = cells 32ks + 16(s/4) + 4j + s%4, as hi + lo
+        half8 pa_hi, pa_lo;
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+            const float pv = P[2 * ks2 + (s >> 2)][s & 3];
+            const _Float16 hi = (_Float16)pv;
+            pa_hi[s] = hi;
+            pa_lo[s] = (_Float16)(pv - (float)hi);
+        }
+        // V scales of the slot pairs (s, s+1): adjacent cells, one dword each
+        half2v sc[4];
+#pragma unroll
+        for (int sp = 0; sp < 4; ++sp) {
+            const int cell = 32 * ks2 + 16 * (sp >> 1) + 4 * j + 2 * (sp & 1);
+            sc[sp] = __builtin_bit_cast(half2v, *(const uint32_t *)&s_vsc[w][c16 >> 2][cell]);
+        }
+#pragma unroll
+        for (int tt = 0; tt < 8; ++tt) {
+            uint32_t vh[4], vl[4];
+#pragma unroll
+            for (int sp = 0; sp < 4; ++sp) {
+                const uint2 x = vraw[ks2][2 * sp], y = vraw[ks2][2 * sp + 1];
+                const uint32_t xs = tt < 4 ? x.x : x.y, ys = tt < 4 ? y.x : y.y;
+                const half2v vi = __builtin_bit_cast(half2v, cvt2_sel(tt & 3, xs, ys));
+                const half2v hi = vi * sc[sp];                              // round to nearest
+                const half2v lo = __builtin_elementwise_fma(vi, sc[sp], -hi); // exact residual
+                vh[sp] = __builtin_bit_cast(uint32_t, hi);
+                vl[sp] = __builtin_bit_cast(uint32_t, lo);
+            }
+            const half8 vb_hi = __builtin_bit_cast(half8, make_uint4(vh[0], vh[1], vh[2], vh[3]));
+            const half8 vb_lo = __builtin_bit_cast(half8, make_uint4(vl[0], vl[1], vl[2], vl[3]));
+            O[tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa_hi, vb_hi, O[tt], 0, 0, 0);
+            O[tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa_hi, vb_lo, O[tt], 0, 0, 0);
+            O[tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa_lo, vb_hi, O[tt], 0, 0, 0);
+        }
+    }
+
+    // ---- write the chunk record ----------------------------------------------
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int head = 4 * j + r;
+        if (head < a.H) {
+            float *dst = a.o + (rec + head) * kD + 8 * c16;
+            float4 v0 = make_float4(O[0][r] * down, O[1][r] * down, O[2][r] * down, O[3][r] * down);
+            float4 v1 = make_float4(O[4][r] * down, O[5][r] * down, O[6][r] * down, O[7][r] * down);
+            *(float4 *)dst = v0;
+            *(float4 *)(dst + 4) = v1;
+        }
+    }
+    if (j == 0 && c16 < a.H) {
+        a.m[rec + c16] = mx;
+        a.l[rec + c16] = lsum;
+    }
+}
+
+} // namespace
+
+hipError_t launch_attn(const AttnArgs &a, hipStream_t stream)
+{
+    dim3 grid(8 * a.blocks_per_xcd), block(64 * kWaves);
+    hipLaunchKernelGGL(attn_kernel, grid, block, 0, stream, a);
+    return hipGetLastError();
+}
+
+} // namespace qsa

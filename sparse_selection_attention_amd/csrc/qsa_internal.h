@@ -1,0 +1,67 @@
+// qsa_internal.h -- declarations shared by the kernels and the C-ABI layer of
+// libqsa.so. Not installed; the public interface is include/qsa.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qsa {
+
+constexpr int kD = 128;       // head dim implemented by this build
+constexpr int kChunk = 64;    // slots per chunk
+constexpr int kGroup = 32;    // dims per fp16 scale
+constexpr int kMaxHeads = 16; // heads fill the 16-wide MFMA tile dimension
+constexpr int kAttnWaves = 4; // (token, chunk) work items per attention workgroup
+constexpr int kMaxCells = 1 << 25; // cache rows addressed with 32-bit byte offsets
+
+struct AttnArgs {
+    const _Float16 *q;        // [T][H][D]
+    const int8_t *kq;         // [n_cells][D]
+    const int8_t *vq;         // [n_cells][D]
+    const uint16_t *ksc;      // [n_cells][D/32] fp16 bits
+    const uint16_t *vsc;      // [n_cells][D/32] fp16 bits
+    const int32_t *ids;       // [T][ids_stride] or nullptr (implicit rows)
+    int64_t ids_stride;
+    int32_t n_cells, pos0, T, H, C;
+    float scale;
+    float *o;                 // [T][C][H][D]
+    float *m;                 // [T][C][H]
+    float *l;                 // [T][C][H]
+    int64_t n_items;          // T * C work items, one 64-lane wave each
+    int32_t n_blocks;         // workgroups that carry work
+    int32_t blocks_per_xcd;   // workgroups each XCD walks through
+};
+
+struct MergeArgs {
+    const float *o, *m, *l;
+    int32_t C, T, H;
+    _Float16 *out;            // [T][H][D]
+};
+
+struct ScoreArgs {
+    const float *q;           // [T][Hs][D]
+    const float *k;           // [n_cells][D]
+    int32_t n_cells, pos0, T, Hs;
+    float scale, dead;
+    float *scores;            // [T][row_stride]
+    int64_t row_stride;
+};
+
+// Part workspace layout: o, then m, then l, each on a 256-byte boundary.
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+inline void part_layout(int64_t T, int64_t H, int64_t D, int64_t C,
+                        size_t *o_off, size_t *m_off, size_t *l_off, size_t *total)
+{
+    size_t o_bytes = align256(size_t(T) * C * H * D * sizeof(float));
+    size_t s_bytes = align256(size_t(T) * C * H * sizeof(float));
+    if (o_off) *o_off = 0;
+    if (m_off) *m_off = o_bytes;
+    if (l_off) *l_off = o_bytes + s_bytes;
+    if (total) *total = o_bytes + 2 * s_bytes;
+}
+
+hipError_t launch_attn(const AttnArgs &a, hipStream_t stream);
+hipError_t launch_merge(const MergeArgs &a, hipStream_t stream);
+hipError_t launch_score(const ScoreArgs &a, hipStream_t stream);
+
+} // namespace qsa

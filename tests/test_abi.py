@@ -1,0 +1,162 @@
+"""C-ABI checks that need no GPU: the library loads, exports what include/*.h
+declares, sizes the part workspace, and rejects bad arguments on the host
+before anything reaches a device."""
+import ctypes
+import glob
+import os
+import re
+
+import pytest
+
+import sparse_selection_attention_amd as qsa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_symbols():
+    names = set()
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        text = open(h).read()
+        names |= set(re.findall(r"QSA_API\s+[^;(]*?\b(qsa_\w+)\s*\(", text))
+    return names
+
+
+def test_library_loads_and_exports_every_declared_symbol():
+    L = qsa.lib()
+    names = declared_symbols()
+    assert {"qsa_attn", "qsa_merge", "qsa_score", "qsa_part_bytes", "qsa_part_offsets",
+            "qsa_last_error"} <= names
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_no_unexpected_exports():
+    out = os.popen("nm -D --defined-only %s" % qsa.LIB_PATH).read()
+    exported = set(re.findall(r"\bT (qsa_\w+)", out))
+    assert exported == declared_symbols()
+
+
+def test_part_layout():
+    T, H, D, C = 1984, 12, 128, 33
+    o, m, l = qsa.qsa_part_offsets(T, H, D, C)
+    assert o == 0
+    assert m == 4 * T * C * H * D                      # already a multiple of 256
+    assert l == m + ((4 * T * C * H + 255) // 256) * 256
+    assert qsa.qsa_part_bytes(T, H, D, C) == l + ((4 * T * C * H + 255) // 256) * 256
+    # same bytes per record as the pages' {max, denominator, output[D]} records
+    assert 4 * T * C * H * (2 + D) <= qsa.qsa_part_bytes(T, H, D, C) < 4 * T * C * H * (2 + D) + 512
+    for T_, H_, C_ in [(1, 1, 1), (3, 5, 7), (17, 16, 2)]:
+        o, m, l = qsa.qsa_part_offsets(T_, H_, 128, C_)
+        assert o % 256 == 0 and m % 256 == 0 and l % 256 == 0
+        assert m >= 4 * T_ * C_ * H_ * 128 and l >= m + 4 * T_ * C_ * H_
+    assert qsa.qsa_part_bytes(-1, 1, 128, 1) == 0
+
+
+FAKE = 0x10000        # a 256-byte aligned host address that is never dereferenced
+
+
+def attn(**kw):
+    a = dict(q=FAKE, kq=FAKE, vq=FAKE, ksc=FAKE, vsc=FAKE, n_cells=100, ids=FAKE, ids_stride=64,
+             pos0=10, T=4, H=12, D=128, scale=0.1, part=FAKE, stream=None)
+    a.update(kw)
+    P = ctypes.c_void_p
+    return qsa.lib().qsa_attn(P(a["q"]), P(a["kq"]), P(a["vq"]), P(a["ksc"]), P(a["vsc"]), a["n_cells"],
+                              P(a["ids"]), a["ids_stride"], a["pos0"], a["T"], a["H"], a["D"], a["scale"],
+                              P(a["part"]), P(a["stream"]))
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(T=-1), qsa.QSA_ERR_ARG),
+    (dict(pos0=-3), qsa.QSA_ERR_ARG),
+    (dict(n_cells=-1), qsa.QSA_ERR_ARG),
+    (dict(H=0), qsa.QSA_ERR_ARG),
+    (dict(H=17), qsa.QSA_ERR_UNSUPPORTED),
+    (dict(D=64), qsa.QSA_ERR_UNSUPPORTED),
+    (dict(D=256), qsa.QSA_ERR_UNSUPPORTED),
+    (dict(ids_stride=0), qsa.QSA_ERR_ARG),
+    (dict(ids_stride=100), qsa.QSA_ERR_ARG),
+    (dict(ids_stride=-64), qsa.QSA_ERR_ARG),
+    (dict(q=None), qsa.QSA_ERR_ARG),
+    (dict(kq=None), qsa.QSA_ERR_ARG),
+    (dict(vq=None), qsa.QSA_ERR_ARG),
+    (dict(ksc=None), qsa.QSA_ERR_ARG),
+    (dict(vsc=None), qsa.QSA_ERR_ARG),
+    (dict(part=None), qsa.QSA_ERR_ARG),
+    (dict(q=FAKE + 8), qsa.QSA_ERR_ARG),
+    (dict(kq=FAKE + 4), qsa.QSA_ERR_ARG),
+    (dict(vq=FAKE + 1), qsa.QSA_ERR_ARG),
+    (dict(ksc=FAKE + 2), qsa.QSA_ERR_ARG),
+    (dict(vsc=FAKE + 4), qsa.QSA_ERR_ARG),
+    (dict(part=FAKE + 128), qsa.QSA_ERR_ARG),
+    (dict(ids=FAKE + 2), qsa.QSA_ERR_ARG),
+    (dict(pos0=2**31 - 2, T=4), qsa.QSA_ERR_ARG),
+])
+def test_attn_rejects_bad_arguments_on_host(kw, status):
+    assert attn(**kw) == status
+    assert qsa.qsa_last_error() != ""
+
+
+def test_zero_tokens_is_a_no_op():
+    # T == 0 returns OK before touching any pointer or device
+    assert attn(T=0, q=None, kq=None, part=None) == qsa.QSA_OK
+    assert qsa.qsa_last_error() == ""
+    P = ctypes.c_void_p
+    assert qsa.lib().qsa_merge(P(None), 5, 0, 12, 128, P(None), P(None)) == qsa.QSA_OK
+    assert qsa.lib().qsa_score(P(None), P(None), 10, 10, 0, 1, 128, 1.0, 0.0, P(None), 10, P(None)) == qsa.QSA_OK
+
+
+@pytest.mark.parametrize("args,status", [
+    ((FAKE, 3, -1, 12, 128, FAKE), qsa.QSA_ERR_ARG),
+    ((FAKE, -1, 2, 12, 128, FAKE), qsa.QSA_ERR_ARG),
+    ((FAKE, 3, 2, 0, 128, FAKE), qsa.QSA_ERR_ARG),
+    ((FAKE, 3, 2, 17, 128, FAKE), qsa.QSA_ERR_UNSUPPORTED),
+    ((FAKE, 3, 2, 12, 96, FAKE), qsa.QSA_ERR_UNSUPPORTED),
+    ((None, 3, 2, 12, 128, FAKE), qsa.QSA_ERR_ARG),
+    ((FAKE, 3, 2, 12, 128, None), qsa.QSA_ERR_ARG),
+    ((FAKE + 64, 3, 2, 12, 128, FAKE), qsa.QSA_ERR_ARG),
+    ((FAKE, 3, 2, 12, 128, FAKE + 2), qsa.QSA_ERR_ARG),
+])
+def test_merge_rejects_bad_arguments_on_host(args, status):
+    P = ctypes.c_void_p
+    part, C, T, H, D, out = args
+    assert qsa.lib().qsa_merge(P(part), C, T, H, D, P(out), P(None)) == status
+    assert qsa.qsa_last_error().startswith("qsa_merge")
+
+
+def score(**kw):
+    a = dict(q=FAKE, k=FAKE, n_cells=100, pos0=10, T=4, Hs=1, D=128, scale=1.0, dead=-1.0, scores=FAKE,
+             row_stride=14)
+    a.update(kw)
+    P = ctypes.c_void_p
+    return qsa.lib().qsa_score(P(a["q"]), P(a["k"]), a["n_cells"], a["pos0"], a["T"], a["Hs"], a["D"],
+                               a["scale"], a["dead"], P(a["scores"]), a["row_stride"], P(None))
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(T=-2), qsa.QSA_ERR_ARG),
+    (dict(pos0=-2), qsa.QSA_ERR_ARG),
+    (dict(Hs=0), qsa.QSA_ERR_ARG),
+    (dict(Hs=17), qsa.QSA_ERR_UNSUPPORTED),
+    (dict(D=64), qsa.QSA_ERR_UNSUPPORTED),
+    (dict(n_cells=13), qsa.QSA_ERR_ARG),
+    (dict(row_stride=13), qsa.QSA_ERR_ARG),
+    (dict(q=None), qsa.QSA_ERR_ARG),
+    (dict(k=None), qsa.QSA_ERR_ARG),
+    (dict(scores=None), qsa.QSA_ERR_ARG),
+    (dict(q=FAKE + 4), qsa.QSA_ERR_ARG),
+    (dict(k=FAKE + 8), qsa.QSA_ERR_ARG),
+    (dict(scores=FAKE + 2), qsa.QSA_ERR_ARG),
+    (dict(T=64 * 65536, pos0=0, n_cells=64 * 65536, row_stride=64 * 65536), qsa.QSA_ERR_ARG),
+])
+def test_score_rejects_bad_arguments_on_host(kw, status):
+    assert score(**kw) == status
+    assert qsa.qsa_last_error().startswith("qsa_score")
+
+
+def test_binding_refuses_host_tensors():
+    import torch
+    q = torch.zeros(2, 1, 128, dtype=torch.float16)
+    kq = torch.zeros(4, 128, dtype=torch.int8)
+    sc = torch.ones(4, 4, dtype=torch.float16)
+    with pytest.raises(ValueError):
+        qsa.qsa_attn(q, kq, kq, sc, sc, None, 2, 0.1, torch.zeros(1 << 16, dtype=torch.uint8))

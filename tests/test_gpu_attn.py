@@ -1,0 +1,286 @@
+"""GPU parity of qsa_attn + qsa_merge against the CPU oracle, through the C ABI.
+
+Covers the five workloads at their full sizes (tokens sampled for the oracle),
+and the bit-exact probes of id and selection handling."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sparse_selection_attention_amd as qsa
+from sparse_selection_attention_amd import synth
+
+from gpu_util import (check_attn_case, check_out, check_records, chunk_magnitude, dev, oracle_token,
+                      oracle_tokens, run_attn, to_dev)
+
+pytestmark = pytest.mark.gpu
+
+
+def _print(*a):
+    print(*a, flush=True)
+
+
+# ---------------------------------------------------------------------------
+# the five workloads
+
+
+def test_tiny_all_tokens():
+    case = synth.tiny()
+    L = case.layers[0]
+    out, o, m, l, C = run_attn(L, case.ids, case.pos0, case.scale)
+    for t in range(case.T):
+        r = oracle_token(L, case.ids, case.pos0, case.scale, t)
+        check_out(out[t], r["out64"], "tiny t=%d" % t)
+        check_records(o[t], m[t], l[t], r, chunk_magnitude(L, case.ids, case.pos0, case.scale, t, C), t, "tiny")
+
+
+@pytest.mark.parametrize("ntok", range(1, 9))
+def test_mtp_decode_window(ntok):
+    case = synth.mtp(ntok)
+    _print("mtp ntok", ntok, check_attn_case(case))
+
+
+def test_prompt_start_explicit():
+    _print("prompt", check_attn_case(synth.prompt_start(), n_sample=16))
+
+
+def test_prompt_start_implicit_rows_match_explicit_bitwise():
+    case = synth.prompt_start()
+    L = case.layers[0]
+    a = run_attn(L, case.ids, case.pos0, case.scale)
+    b = run_attn(L, None, case.pos0, case.scale, implicit=True)
+    assert a[4] == b[4]
+    assert np.array_equal(a[0].view(np.uint16), b[0].view(np.uint16))
+    assert np.array_equal(a[2].view(np.uint32), b[2].view(np.uint32))
+    assert np.array_equal(a[3].view(np.uint32), b[3].view(np.uint32))
+    valid = ~np.isinf(a[2])                      # o is written only for non-empty chunks
+    assert np.array_equal(a[1].view(np.uint32)[valid], b[1].view(np.uint32)[valid])
+
+
+def test_prompt_start_implicit_vs_oracle():
+    _print("prompt implicit", check_attn_case(synth.prompt_start(), n_sample=12, implicit=True))
+
+
+def test_mid_context_three_layers():
+    _print("mid", check_attn_case(synth.mid(layers=3), n_sample=12))
+
+
+def test_long_context_three_layers():
+    _print("long", check_attn_case(synth.long_ctx(layers=3), n_sample=12))
+
+
+@pytest.mark.parametrize("variant", ["signed_zero", "cancel"])
+def test_long_context_edge_variants(variant):
+    case = synth.long_ctx(layers=1, variant=variant)
+    L = case.layers[0]
+    out, o, m, l, C = run_attn(L, case.ids, case.pos0, case.scale)
+    toks = [0, 4, 1980] if variant == "signed_zero" else [1, 5, 1981]
+    heads = [0, 6] if variant == "signed_zero" else list(range(12))
+    refs = oracle_tokens(L, case.ids, case.pos0, case.scale, toks + [2, 3])
+    for t in toks:
+        row = case.ids[t]
+        cells = row[row >= 0]
+        mean = (L.vq[cells].astype(np.float64) * np.repeat(L.vsc[cells].astype(np.float64), 32, axis=1)).mean(0)
+        for h in heads:
+            assert np.all(m[t, :, h] == 0.0), "scores must be exactly +-0"
+            assert np.all(l[t, :32, h] == 64.0) and l[t, 32, h] == 3.0
+            check_out(out[t, h], mean, "%s t=%d h=%d" % (variant, t, h))
+        check_out(out[t], refs[t]["out64"], "%s t=%d" % (variant, t))
+    for t in (2, 3):                             # untouched tokens keep plain parity
+        check_out(out[t], refs[t]["out64"], "%s t=%d" % (variant, t))
+
+
+# ---------------------------------------------------------------------------
+# bit-exact probes of ids and selection
+
+
+def probe_case(T=150, H=12, n_cells=700, C=5, seed=1, p_poison=0.3):
+    rng = np.random.default_rng(seed)
+    L = synth.make_layer(seed, 0, T, H, n_cells)
+    pos0 = n_cells - T
+    ids = np.full((T, 64 * C), -1, dtype=np.int32)
+    for t in range(T):
+        p = pos0 + t
+        row = rng.integers(0, p + 1, 64 * C)
+        row[rng.random(64 * C) < p_poison] = -1
+        bad = rng.random(64 * C) < 0.03
+        row[bad] = rng.choice([n_cells, n_cells + 999, -2, -(2 ** 31)], bad.sum())
+        ids[t] = row
+    ids[3, 64:128] = -1                          # an empty chunk
+    ids[7, :] = -1                               # an empty row
+    ids[9, -64:] = -1
+    ids[9, -64 + 17] = 5                         # a lone cell in the ragged last chunk
+    return L, ids, pos0
+
+
+def valid_counts(ids, n_cells):
+    T, S = ids.shape
+    v = (ids >= 0) & (ids < n_cells)
+    return v.reshape(T, S // 64, 64).sum(axis=2)
+
+
+def test_uniform_probe_records_are_exact():
+    """q = 1, K = 0, unit V scales: l counts the valid slots, o sums the selected V rows."""
+    L, ids, pos0 = probe_case()
+    L.q[:] = 1.0
+    L.kq[:] = 0
+    L.vsc[:] = 1.0
+    n_cells = L.kq.shape[0]
+    out, o, m, l, C = run_attn(L, ids, pos0, np.float32(0.3))
+    cnt = valid_counts(ids, n_cells)
+    H = L.q.shape[1]
+    assert np.array_equal(l, np.repeat(cnt[:, :, None], H, axis=2).astype(np.float32))
+    ne = cnt > 0
+    assert np.all(m[ne] == 0.0) and np.all(m[~ne] == -np.inf)
+    for t in range(ids.shape[0]):
+        for k in range(C):
+            r = ids[t, 64 * k: 64 * k + 64]
+            cells = r[(r >= 0) & (r < n_cells)]
+            if len(cells):
+                s = L.vq[cells].astype(np.int64).sum(0).astype(np.float32)
+                assert np.array_equal(o[t, k], np.broadcast_to(s, (H, 128))), (t, k)
+
+
+def test_uniform_probe_full_long_selection():
+    """The same probe over the full long-context selection: every chunk's count is exact."""
+    case = synth.long_ctx(layers=1)
+    L = case.layers[0]
+    L.q[:] = 1.0
+    L.kq[:] = 0
+    L.vsc[:] = 1.0
+    out, o, m, l, C = run_attn(L, case.ids, case.pos0, case.scale)
+    cnt = valid_counts(case.ids, case.n_cells)
+    assert np.array_equal(l, np.repeat(cnt[:, :, None], 12, axis=2).astype(np.float32))
+    assert np.all(m == 0.0)
+    for t in (0, 777, 1983):
+        for k in (0, 17, 32):
+            r = case.ids[t, 64 * k: 64 * k + 64]
+            s = L.vq[r[r >= 0]].astype(np.int64).sum(0).astype(np.float32)
+            assert np.array_equal(o[t, k], np.broadcast_to(s, (12, 128)))
+
+
+def test_k_address_probe_max_is_exact():
+    L, ids, pos0 = probe_case(H=3, seed=2)
+    d0 = 93
+    n_cells = L.kq.shape[0]
+    L.q[:] = 0.0
+    L.q[:, :, d0] = 1.0
+    L.ksc[:] = 1.0
+    L.kq[:, d0] = ((np.arange(n_cells) * 2654435761) % 255 - 127).astype(np.int8)
+    out, o, m, l, C = run_attn(L, ids, pos0, np.float32(1.0))
+    for t in range(ids.shape[0]):
+        for k in range(C):
+            r = ids[t, 64 * k: 64 * k + 64]
+            cells = r[(r >= 0) & (r < n_cells)]
+            want = L.kq[cells, d0].astype(np.float32).max() if len(cells) else -np.inf
+            assert np.all(m[t, k] == want), (t, k)
+
+
+def test_one_cell_selection_is_bitwise_dequantised_v():
+    T, H, n_cells = 64, 12, 300
+    L = synth.make_layer(4, 0, T, H, n_cells)
+    rng = np.random.default_rng(0)
+    ids = np.full((T, 192), -1, dtype=np.int32)
+    cells = rng.integers(0, n_cells - T, T)
+    slots = rng.integers(0, 192, T)
+    ids[np.arange(T), slots] = cells
+    out, o, m, l, C = run_attn(L, ids, n_cells - T, synth.SCALE_1_SQRT_128)
+    v = (L.vq[cells].astype(np.float64) * np.repeat(L.vsc[cells].astype(np.float64), 32, axis=1))
+    want = v.astype(np.float16)
+    assert np.array_equal(out.view(np.uint16), np.repeat(want[:, None, :], H, axis=1).view(np.uint16))
+
+
+def test_poison_and_unselected_data_do_not_matter():
+    L, ids, pos0 = probe_case(seed=3)
+    n_cells = L.kq.shape[0]
+    a = run_attn(L, ids, pos0, synth.SCALE_1_SQRT_128)
+    used = np.zeros(n_cells, bool)
+    v = ids[(ids >= 0) & (ids < n_cells)]
+    used[v] = True
+    L2 = synth.Layer(L.q.copy(), L.kq.copy(), L.vq.copy(), L.ksc.copy(), L.vsc.copy())
+    L2.kq[~used] = 127
+    L2.vq[~used] = -127
+    L2.ksc[~used] = 60000.0
+    L2.vsc[~used] = 1000.0
+    ids2 = ids.copy()
+    ids2[(ids2 < 0) | (ids2 >= n_cells)] = -1
+    b = run_attn(L2, ids2, pos0, synth.SCALE_1_SQRT_128)
+    assert np.array_equal(a[0].view(np.uint16), b[0].view(np.uint16))
+    assert np.array_equal(a[2].view(np.uint32), b[2].view(np.uint32))
+    assert np.array_equal(a[3].view(np.uint32), b[3].view(np.uint32))
+
+
+def test_empty_chunk_and_row():
+    L, ids, pos0 = probe_case(seed=4)
+    out, o, m, l, C = run_attn(L, ids, pos0, synth.SCALE_1_SQRT_128, part_fill=0x7F)
+    sentinel = np.array([0x7F7F7F7F], np.uint32).view(np.float32)[0]
+    assert np.all(m[3, 1] == -np.inf) and np.all(l[3, 1].view(np.uint32) == 0)
+    assert np.all(o[3, 1] == sentinel)            # o of an empty chunk is not written
+    assert np.all(m[7] == -np.inf)
+    assert np.all(out[7].view(np.uint16) == 0)    # a row with no valid slot is +0
+    r = oracle_token(L, ids, pos0, synth.SCALE_1_SQRT_128, 9)
+    check_out(out[9], r["out64"], "ragged lone cell")
+
+
+def test_run_to_run_determinism():
+    L, ids, pos0 = probe_case(seed=5)
+    a = run_attn(L, ids, pos0, synth.SCALE_1_SQRT_128)
+    b = run_attn(L, ids, pos0, synth.SCALE_1_SQRT_128)
+    for x, y in zip(a[:4], b[:4]):
+        assert np.array_equal(x.view(np.uint8), y.view(np.uint8))
+
+
+def test_probe_case_vs_oracle_all_tokens():
+    L, ids, pos0 = probe_case(seed=6)
+    out, o, m, l, C = run_attn(L, ids, pos0, synth.SCALE_1_SQRT_128)
+    refs = oracle_tokens(L, ids, pos0, synth.SCALE_1_SQRT_128, list(range(ids.shape[0])))
+    for t, r in refs.items():
+        check_out(out[t], r["out64"], "probe t=%d" % t)
+        check_records(o[t], m[t], l[t], r, chunk_magnitude(L, ids, pos0, synth.SCALE_1_SQRT_128, t, C), t, "probe")
+
+
+@pytest.mark.parametrize("T,H,n_cells,pos0", [(1, 1, 1, 0), (1, 16, 65, 64), (5, 7, 130, 125), (70, 16, 200, 130),
+                                             (33, 2, 64, 31)])
+def test_edge_shapes_implicit_rows(T, H, n_cells, pos0):
+    L = synth.make_layer(T + H, 0, T, H, n_cells)
+    out, o, m, l, C = run_attn(L, None, pos0, synth.SCALE_1_SQRT_128, implicit=True)
+    for t in range(T):
+        r = oracle_token(L, None, pos0, synth.SCALE_1_SQRT_128, t)
+        check_out(out[t], r["out64"], "edge t=%d" % t)
+        check_records(o[t], m[t], l[t], r, chunk_magnitude(L, None, pos0, synth.SCALE_1_SQRT_128, t, C), t, "edge")
+
+
+def test_large_and_tiny_scales():
+    """V scales far from the configs' range, and large logits: no overflow, parity holds."""
+    L, ids, pos0 = probe_case(T=40, seed=7)
+    base = L.vsc.astype(np.float32)
+    L.vsc[:] = (base * 10000).astype(np.float16)                       # up to 200
+    L.vsc[::3] = (base[::3] * 1e-3).astype(np.float16)                 # fp16 subnormals
+    L.ksc[:5] = np.float16(2.0 ** -24)                                 # subnormal scales
+    L.q[:] = (L.q.astype(np.float32) * 40).astype(np.float16)           # logits of several hundred
+    out, o, m, l, C = run_attn(L, ids, pos0, np.float32(1.0))
+    refs = oracle_tokens(L, ids, pos0, np.float32(1.0), list(range(40)))
+    for t, r in refs.items():
+        scale_out = max(1.0, float(np.abs(r["out64"]).max()))
+        g = out[t].astype(np.float64)
+        assert np.all(np.isfinite(g[np.isfinite(r["out64"])]))
+        assert np.abs(g - r["out64"]).max() <= 2e-3 * scale_out
+
+
+def test_stream_argument_is_honoured():
+    case = synth.tiny()
+    L = case.layers[0]
+    s = torch.cuda.Stream()
+    q, kq, vq, ksc, vsc = (to_dev(x) for x in (L.q, L.kq, L.vq, L.ksc, L.vsc))
+    ids = to_dev(case.ids)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        part = qsa.alloc_part(16, 2, 128, 1)
+        out = torch.empty(16, 2, 128, dtype=torch.float16, device=dev())
+        qsa.qsa_attn(q, kq, vq, ksc, vsc, ids, 0, float(case.scale), part, stream=s)
+        qsa.qsa_merge(part, 1, out, stream=s)
+    s.synchronize()
+    ref, _, _ = oracle.attn(L.q, L.kq, L.vq, L.ksc, L.vsc, case.ids, 0, case.scale)
+    check_out(out.cpu().numpy(), ref, "stream")
