@@ -1,7 +1,7 @@
 /*
  * qsa.h -- C ABI of libqsa.so: explicit-selection attention over an int8 K/V
- * cache shared by all query heads, its max-first chunk merge, and causal q.K
- * scores, on AMD Instinct MI355X (gfx950).
+ * cache shared by all query heads, the merge of its chunk records, and causal
+ * q.K scores, on AMD Instinct MI355X (gfx950).
  *
  * Every pointer argument is a DEVICE pointer to memory the caller owns. The
  * library allocates nothing, keeps no per-call state and is safe to call from
@@ -53,11 +53,12 @@ typedef enum {
  *
  * Defined by "round 11 track b: qsa attention and score", section
  * "implementation and evaluator" (int8 K/V rows addressed by selected cell
- * ids, four scale groups per row, incomplete 64-cell chunks, empty slots that
- * contribute nothing, the partial buffer written before the merge), and by
- * "round 5 track b: cached residual norms and fused mtp attention", section
- * "mtp attention" (per-64-cell chunk arithmetic with per-chunk maxima and
- * denominators, one V load per dim per cell for all heads).
+ * ids, one scale per quarter of a row, a last chunk that may be partly filled,
+ * empty slots that add nothing, and chunk partials that are stored before they
+ * are merged), and by "round 5 track b: cached residual norms and fused mtp
+ * attention", section "mtp attention" (chunks of 64 cells, each with its own
+ * maximum and denominator; each V value read once per cell and shared by all
+ * heads).
  *
  * For each query token t (cache position p = pos0 + t), each chunk k of its id
  * row (slots 64k .. 64k+63) and each head h < H, with the valid slots j of the
@@ -97,8 +98,9 @@ QSA_API qsa_status qsa_attn(const void *q, const int8_t *kq, const int8_t *vq,
  * qsa_merge -- max-first merge of chunk records into fp16 output.
  *
  * Defined by "round 5 track b: cached residual norms and fused mtp attention",
- * sections "preflight / ownership" and "mtp attention" (the max-first chunk
- * merge). For each token t and head h, over chunks with m_k != -inf:
+ * sections "preflight / ownership" and "mtp attention" (chunk records are
+ * combined relative to the largest chunk maximum). For each token t and head
+ * h, over chunks with m_k != -inf:
  *   M = max_k m_k,  w_k = exp(m_k - M),  L = sum_k w_k l_k,
  *   out[t][h][d] = fp16_rne( sum_k w_k o_k[d] / L )
  * A (t, h) with no such chunk gets +0 in every dim. Records with m = -inf are
@@ -114,9 +116,10 @@ QSA_API qsa_status qsa_merge(const void *part, int32_t n_chunks, int32_t T, int3
  * qsa_score -- fp32 q.K scores over causal cells with a dead-key tail.
  *
  * Defined by "round 11 track b: qsa attention and score", sections
- * "implementation and evaluator" (scores over causal cells, a scalar dead-key
- * tail, beyond-causal cells left untouched) and "score: valid negative result"
- * (64-cell tiles, a head reduction). For row t (p = pos0 + t):
+ * "implementation and evaluator" (causal cells get scores, a single constant
+ * marks the cells just past the causal edge, cells after those are not
+ * written) and "score: valid negative result" (64-cell tiles, a sum over
+ * heads). For row t (p = pos0 + t):
  *   scores[t][c] = scale * sum_{h < Hs} sum_d q[t][h][d] * k[c][d]   for c <= p
  *   scores[t][c] = dead       for p < c < min(64 * ceil((p + 1) / 64), row_stride)
  * and every later cell of the row is left untouched.

@@ -17,30 +17,32 @@
  *    64-slot chunk k of the token's id row, per head h:
  *      valid slots   : ids with 0 <= id < n_cells; -1 marks a slot that
  *                      contributes nothing ("round 11 track b: qsa attention and
- *                      score", section "boundaries and provenance": implicit
- *                      rows poison ids with -1; section "implementation and
- *                      evaluator": incomplete 64-cell chunks);
+ *                      score", section "boundaries and provenance": unused id
+ *                      slots carry -1; section "implementation and evaluator":
+ *                      the last chunk of a row may be only partly filled);
  *      dequantise    : k_d = kq[c][d] * ksc[c][d/32], v_d = vq[c][d] * vsc[c][d/32]
  *                      (int8 rows, one fp16 scale per 32-dim group; same page,
- *                      section "implementation and evaluator": four scale
- *                      groups per K row);
+ *                      section "implementation and evaluator": a K row has one
+ *                      scale per quarter of its dims);
  *      scaled dot    : S_j = scale * sum_d q[t][h][d] * k_d;
  *      chunk record  : m = max_j S_j, p_j = exp(S_j - m), l = sum_j p_j,
  *                      o[d] = sum_j p_j * v_{c_j, d}; a chunk with no valid slot
  *                      gets m = -inf, l = +0 and its o is left as it was
  *                      ("round 5 track b: cached residual norms and fused mtp
- *                      attention", section "mtp attention": per-64-cell chunk
- *                      arithmetic, per-chunk maxima and denominators).
- *  qso_merge -- max-first merge of a token's chunk records per head
- *    (same page and section: "max-first chunk merge"):
+ *                      attention", section "mtp attention": each 64-cell chunk
+ *                      keeps its own maximum and denominator).
+ *  qso_merge -- merge of a token's chunk records per head, taken relative to
+ *    the largest chunk maximum (same page and section):
  *      M = max_k m_k over chunks with m_k != -inf, w_k = exp(m_k - M),
  *      L = sum_k w_k l_k, O[d] = sum_k w_k o_k[d], out = O / L,
  *      fp16 by round-to-nearest-even. A token with no valid slot gets +0.
  *  qso_score -- causal scores ("round 11 track b: qsa attention and score",
  *    sections "implementation and evaluator" and "score: valid negative
- *    result"): scores[t][c] = scale * sum_h sum_d q[t][h][d] * k[c][d] for
- *    c <= p; the rest of the 64-cell tile that holds cell p (and lies inside
- *    the row) gets the scalar `dead`; every later cell is left as it was.
+ *    result": causal cells get scores, a constant marks the cells just past
+ *    the causal edge, later cells are not written). Here: scores[t][c] =
+ *    scale * sum_h sum_d q[t][h][d] * k[c][d] for c <= p; the rest of the
+ *    64-cell tile that holds cell p (and lies inside the row) gets `dead`;
+ *    every later cell is left as it was.
  */
 #include <math.h>
 #include <stddef.h>

@@ -2,10 +2,11 @@
 //
 // What is computed follows "round 11 track b: qsa attention and score",
 // section "implementation and evaluator" (int8 K/V rows gathered by selected
-// cell id, four scale groups per K row, incomplete 64-cell chunks, empty slots
-// that contribute nothing) and "round 5 track b: cached residual norms and
-// fused mtp attention", section "mtp attention" (per-chunk max, denominator and
-// partial output; one V load per dim per cell for all heads).
+// cell id, one scale per quarter of a K row, a last chunk that may be partly
+// filled, empty slots that add nothing) and "round 5 track b: cached residual
+// norms and fused mtp attention", section "mtp attention" (a max, a
+// denominator and a partial output per chunk; each V value read once per cell
+// for all heads).
 //
 // Design on CDNA4. One 64-lane wave owns one (token, chunk) pair:
 //   * lane c reads slot c's id; a ballot gives the chunk's valid mask;
@@ -14,7 +15,7 @@
 //   * QK: v_mfma_f32_16x16x32_f16 with A = K rows (16 cells x 32 dims of one
 //     scale group, int8 converted exactly to fp16) and B = q (32 dims x 16
 //     heads), giving one fp32 partial per scale group that is then weighted by
-//     the cell's group scale -- the four per-group partials of the pages;
+//     the cell's group scale, as the pages build the score from partials;
 //   * the chunk max and denominator are lane-local folds plus two cross-row
 //     exchanges, because the score tile already holds one head per lane column;
 //   * PV: v_mfma_f32_16x16x32_f16 with A = p (heads x 32 cells) straight from

@@ -1,9 +1,9 @@
 // qsa_merge.hip -- max-first merge of chunk records into fp16 output on gfx950.
 //
 // Follows "round 5 track b: cached residual norms and fused mtp attention",
-// sections "preflight / ownership" and "mtp attention" (the max-first chunk
-// merge after per-64-cell chunk arithmetic). For token t and head h, over the
-// chunks whose max is finite:
+// sections "preflight / ownership" and "mtp attention": the per-chunk records of
+// 64-cell chunks are combined relative to the largest chunk maximum. For token
+// t and head h, over the chunks whose max is finite:
 //   M = max_k m_k, w_k = exp(m_k - M), L = sum_k w_k l_k,
 //   out[d] = fp16_rne(sum_k w_k o_k[d] / L),
 // and +0 when no chunk of the row had a valid slot. Records with m = -inf are

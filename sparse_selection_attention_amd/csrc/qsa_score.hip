@@ -1,9 +1,10 @@
 // qsa_score.hip -- fp32 causal q.K scores with a dead-key tail on gfx950.
 //
 // Follows "round 11 track b: qsa attention and score", sections
-// "implementation and evaluator" (scores over causal cells, a scalar dead-key
-// tail, beyond-causal cells untouched) and "score: valid negative result"
-// (64 x 64 score tiles over a 128-deep contraction, a reduction over heads).
+// "implementation and evaluator" (causal cells get scores, one constant marks
+// the cells just past the causal edge, later cells are not written) and
+// "score: valid negative result" (64 x 64 score tiles over a 128-deep
+// contraction, summed over heads).
 // For row t (p = pos0 + t):
 //   scores[t][c] = scale * sum_h sum_d q[t][h][d] * k[c][d]      c <= p
 //   scores[t][c] = dead        p < c < min(64 * ceil((p + 1) / 64), row_stride)

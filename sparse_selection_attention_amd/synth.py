@@ -6,12 +6,12 @@ and the HIP kernels are fed the same bytes.
 
 Workloads follow the pages' descriptions of their test data:
   * "round 11 track b: qsa attention and score", section "boundaries and
-    provenance": seed 5, random signed int8 caches, finite positive fp16
-    scales, fp16 queries, explicit ids that are evenly spaced unique causal
-    cells, deterministic random fp32 inputs for the score kernel;
+    provenance": seed 5; signed int8 K/V caches drawn at random; positive,
+    finite fp16 scales; fp16 queries; selected ids spread evenly over the
+    causal cells without repeats; random fp32 inputs for the score kernel;
   * "round 5 track b: cached residual norms and fused mtp attention", section
-    "mtp attention": the decode window is 64 sink cells, 256 previous local
-    cells and the current cell (321 cells, six 64-cell chunks).
+    "mtp attention": the decode window is 64 sink cells, the 256 cells before
+    the current one, and the current cell (321 cells, six 64-cell chunks).
 
 Random numbers come from SplitMix64 (Steele, Lea and Flood, "Fast splittable
 pseudorandom number generators", OOPSLA 2014) in its counter form: the i-th
@@ -107,7 +107,7 @@ def causal_all_ids(pos0: int, T: int, stride: int) -> np.ndarray:
 
 
 def evenly_spaced_ids(pos0: int, T: int, K: int) -> np.ndarray:
-    """Up to K evenly spaced unique causal cells per row, padded with -1.
+    """Up to K causal cells per row, evenly spaced and without repeats, padded with -1.
 
     Row t (p = pos0 + t) holds every cell 0..p when p + 1 <= K, otherwise
     floor(j * p / (K - 1)) for j = 0..K-1: ascending, unique (the step p/(K-1)
