@@ -126,8 +126,7 @@ qsa_status qsa_attn(const void *q, const int8_t *kq, const int8_t *vq,
         return fail(QSA_ERR_ARG, "qsa_attn: misaligned pointer (q, kq, vq: 16 B; ksc, vsc: 8 B; "
                                  "part: 256 B; ids: 4 B)");
     const int64_t C = ids ? ids_stride / QSA_CHUNK : ((int64_t)pos0 + T + QSA_CHUNK - 1) / QSA_CHUNK;
-    const int64_t n_items = (int64_t)T * C;
-    const int64_t n_blocks = (n_items + qsa::kAttnWaves - 1) / qsa::kAttnWaves;
+    const int64_t n_blocks = (C + qsa::kAttnWaves - 1) / qsa::kAttnWaves * T;   // (chunk group, token)
     const int64_t per_xcd = (n_blocks + 7) / 8;
     if (C > INT32_MAX || per_xcd * 8 > INT32_MAX)
         return fail(QSA_ERR_ARG, "qsa_attn: T * chunks too large for one launch");
@@ -155,7 +154,6 @@ qsa_status qsa_attn(const void *q, const int8_t *kq, const int8_t *vq,
     a.o = reinterpret_cast<float *>(pb + o_off);
     a.m = reinterpret_cast<float *>(pb + m_off);
     a.l = reinterpret_cast<float *>(pb + l_off);
-    a.n_items = n_items;
     a.n_blocks = (int32_t)n_blocks;
     a.blocks_per_xcd = (int32_t)per_xcd;
     return launched(qsa::launch_attn(a, static_cast<hipStream_t>(stream)), "qsa_attn");

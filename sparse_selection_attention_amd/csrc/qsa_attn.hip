@@ -8,10 +8,19 @@
 // denominator and a partial output per chunk; each V value read once per cell
 // for all heads).
 //
-// Design on CDNA4. One 64-lane wave owns one (token, chunk) pair:
+// Design on CDNA4. A workgroup owns four consecutive chunks of one query token,
+// one 64-lane wave per chunk:
 //   * lane c reads slot c's id; a ballot gives the chunk's valid mask;
 //   * the 64 cells' K and V rows are read once for all heads: MFMA tiles put the
 //     heads (up to 16) on one tile dimension and the cells on the other;
+//   * gathers are shaped for the texture unit, whose cost grows with the number
+//     of distinct rows each group of four lanes touches: K rows are copied into
+//     LDS with direct-to-LDS loads of 16 bytes per lane, eight lanes per row,
+//     and read back in MFMA operand order; V rows are read four full rows per
+//     instruction straight into the PV operand registers; the token's q is
+//     copied into LDS once per workgroup and shared by its four waves;
+//   * the K tile and the q rows are XOR-swizzled in 16-byte granules so that
+//     the operand reads hit distinct LDS banks;
 //   * QK: v_mfma_f32_16x16x32_f16 with A = K rows (16 cells x 32 dims of one
 //     scale group, int8 converted exactly to fp16) and B = q (32 dims x 16
 //     heads), giving one fp32 partial per scale group that is then weighted by
@@ -23,41 +32,43 @@
 //     are split into fp16 high and low parts and contracted as
 //     hi*hi + hi*lo + lo*hi, so the products carry about 22 bits:
 //       - vq * vsc has at most 18 significant bits, so V = V_hi + V_lo exactly,
-//         with V_lo formed by one fp16 fma; the V scales of the chunk are first
-//         multiplied by a common power of two so the largest lies in [1, 2),
-//         which keeps vq * vsc inside fp16 range, and that exact power of two is
-//         taken back out of the fp32 result;
+//         with V_lo formed by one fp16 fma. When a chunk's largest V scale
+//         reaches 2^9 (so vq * vsc could leave fp16 range) its V scales are
+//         first multiplied by a common power of two that brings the largest
+//         into [1, 2), and that exact power of two is taken back out of the
+//         fp32 result; smaller scales are used as they are;
 //       - p = P_hi + P_lo to within 2^-22 relative;
 //     a single fp16 rounding of p and of v would cost up to 2^-12 |v| per
 //     term, which is too coarse when a chunk holds a few cells whose values
 //     nearly cancel;
 //   * int8 bytes become fp16 with one SDWA conversion each, the byte picked
 //     straight out of the loaded dword.
-// Work items are ordered chunk-major (all tokens of chunk 0, then chunk 1, ...)
-// and each XCD walks a contiguous range of them, so the cells one XCD gathers
-// stay within a narrow band of the cache and are served from its own L2.
+// Workgroups are ordered by chunk group first (all tokens of chunks 0-3, then
+// chunks 4-7, ...) and each XCD walks a contiguous range of them, so the cells
+// one XCD gathers stay within a narrow band of the cache, served from its L2.
 #include "qsa_internal.h"
 
 namespace qsa {
 namespace {
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 
-constexpr int kWaves = kAttnWaves;         // waves (work items) per workgroup
+constexpr int kWaves = kAttnWaves;         // chunks (one per wave) per workgroup
 constexpr float kLog2e = 1.4426950408889634f;
+
+// LDS layout of one workgroup (dynamic size: the q rows depend on H)
+constexpr int kKTileBytes = kChunk * kD;                 // 8 KB of K rows per wave
+constexpr int kWaveBytes = kKTileBytes + kChunk * 8      // K tile, K scales (fp16 x 4)
+                           + kChunk * 8 + kChunk * 4;    // V scales (group-major), cell ids
+constexpr int attn_lds_bytes(int H) { return kWaves * kWaveBytes + H * kD * 2; }
+
+typedef __attribute__((address_space(3))) void lds_void;
 
 __device__ inline float half_bits_to_float(uint32_t bits16)
 {
     return (float)__builtin_bit_cast(_Float16, (uint16_t)bits16);
-}
-
-__device__ inline uint32_t wave_max_u32(uint32_t x)
-{
-#pragma unroll
-    for (int s = 32; s >= 1; s >>= 1)
-        x = max(x, (uint32_t)__shfl_xor((int)x, s, 64));
-    return x;
 }
 
 // int8 -> fp16 (exact) with SDWA: byte BA of x into the low half, byte BB of y
@@ -103,11 +114,8 @@ __device__ inline half8 i8x8_to_half8(uint2 v)
     QSA_CVT2(b, v.x, 2, v.x, 3);
     QSA_CVT2(c, v.y, 0, v.y, 1);
     QSA_CVT2(d, v.y, 2, v.y, 3);
-    uint4 u = make_uint4(a, b, c, d);
-    return __builtin_bit_cast(half8, u);
+    return __builtin_bit_cast(half8, make_uint4(a, b, c, d));
 }
-
-typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 
 __device__ inline void wave_sync_lds()
 {
@@ -116,11 +124,18 @@ __device__ inline void wave_sync_lds()
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// K tile: row r (a cell of the chunk) holds 8 granules of 16 bytes; logical
+// granule lg sits at physical granule lg ^ ((r >> 1) & 7). Rows of equal parity
+// then spread over all eight granule positions, so the sixteen rows read by one
+// MFMA operand load fall on distinct banks.
+__device__ inline int ktile_offset(int row, int lg) { return row * kD + ((lg ^ ((row >> 1) & 7)) << 4); }
+
+// q rows: head h holds 16 granules; logical granule lg sits at lg ^ (h & 15).
+__device__ inline int qrow_offset(int h, int lg) { return h * (kD * 2) + ((lg ^ (h & 15)) << 4); }
+
 __global__ __launch_bounds__(64 * kWaves) void attn_kernel(AttnArgs a)
 {
-    __shared__ float4 s_ksc[kWaves][kChunk];        // scale * ksc of each cell, fp32
-    __shared__ uint16_t s_vsc[kWaves][4][kChunk];   // group-major, so adjacent cells pair up
-    __shared__ int32_t s_id[kWaves][kChunk];
+    extern __shared__ __align__(16) uint8_t lds[];
 
     const int lane = threadIdx.x & 63;
     const int w = threadIdx.x >> 6;
@@ -130,27 +145,82 @@ __global__ __launch_bounds__(64 * kWaves) void attn_kernel(AttnArgs a)
     // each XCD (workgroup id mod 8) walks a contiguous range of workgroups
     const int lb = (blockIdx.x & 7) * a.blocks_per_xcd + (blockIdx.x >> 3);
     if (lb >= a.n_blocks)
-        return;
-    const int64_t item = (int64_t)lb * kWaves + w;
-    if (item >= a.n_items)
-        return;
-    const int k = (int)(item / a.T);
-    const int t = (int)(item - (int64_t)k * a.T);
+        return;                     // uniform over the workgroup
+    const int kg = lb / a.T;
+    const int t = lb - kg * a.T;
+    const int k = kWaves * kg + w;
+    const bool has_chunk = k < a.C;
     const int p = a.pos0 + t;
 
+    uint8_t *ktile = lds + w * kWaveBytes;
+    uint2 *s_ksc = (uint2 *)(ktile + kKTileBytes);                      // [64] x 4 fp16
+    uint16_t *s_vsc = (uint16_t *)(ktile + kKTileBytes + kChunk * 8);   // [4][64] fp16
+    int32_t *s_id = (int32_t *)(ktile + kKTileBytes + kChunk * 16);     // [64]
+    uint8_t *qrows = lds + kWaves * kWaveBytes;                         // [H][256 B]
+
+    // ---- the token's q rows into LDS, once for the workgroup ---------------
+    // wave w copies granules 64w .. 64w+63 of the H rows of 16 granules
+    {
+        const int gi = 64 * w + lane;            // destination granule
+        const int h = gi >> 4, phys = gi & 15;
+        if (h < a.H) {
+            const int lg = phys ^ (h & 15);
+            const _Float16 *src = a.q + ((int64_t)t * a.H + h) * kD + 8 * lg;
+            __builtin_amdgcn_global_load_lds((const void *)src, (lds_void *)(qrows + 1024 * w), 16, 0, 0);
+        }
+    }
+
     // ---- ids and the valid mask --------------------------------------------
-    const int64_t slot = (int64_t)k * kChunk + lane;
-    int32_t id;
-    if (a.ids)
-        id = a.ids[(int64_t)t * a.ids_stride + slot];
-    else
-        id = slot <= p ? (int32_t)slot : -1;
+    int32_t id = -1;
+    if (has_chunk) {
+        const int64_t slot = (int64_t)k * kChunk + lane;
+        if (a.ids)
+            id = a.ids[(int64_t)t * a.ids_stride + slot];
+        else
+            id = slot <= p ? (int32_t)slot : -1;
+    }
     const bool valid = (uint32_t)id < (uint32_t)a.n_cells;
     const int32_t sid = valid ? id : 0;
     const uint64_t mask = __ballot(valid);
+    const bool work = mask != 0;                 // uniform over the wave
 
+    // ---- issue every gather of the chunk at once -----------------------------
+    s_id[lane] = sid;
+    wave_sync_lds();
+    uint2 ks = make_uint2(0u, 0u), vs = make_uint2(0u, 0u);
+    uint2 vraw[2][8];
+    if (work) {
+        if (valid) {
+            ks = *(const uint2 *)(a.ksc + (int64_t)sid * 4);
+            vs = *(const uint2 *)(a.vsc + (int64_t)sid * 4);
+        }
+        // K rows into the tile: instruction s writes granules 64s .. 64s+63,
+        // i.e. rows 8s .. 8s+7, eight lanes per row
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+            const int row = 8 * s + (lane >> 3);
+            const int lg = (lane & 7) ^ ((row >> 1) & 7);
+            const int8_t *src = a.kq + ((uint32_t)s_id[row] * kD + 16 * lg);   // n_cells * 128 < 2^32
+            __builtin_amdgcn_global_load_lds((const void *)src, (lds_void *)(ktile + 1024 * s), 16, 0, 0);
+        }
+        // V: slot s of k-step ks is cell 32ks + 16(s/4) + 4j + s%4 -- the cells
+        // whose scores this lane holds -- and the lane reads dims 8*c16 .. +7
+#pragma unroll
+        for (int ks2 = 0; ks2 < 2; ++ks2)
+#pragma unroll
+            for (int s = 0; s < 8; ++s) {
+                const int cell = 32 * ks2 + 16 * (s >> 2) + 4 * j + (s & 3);
+                vraw[ks2][s] = *(const uint2 *)(a.vq + ((uint32_t)s_id[cell] * kD + 8 * c16));
+            }
+    }
+    // direct-to-LDS copies (q, K) complete, then the whole workgroup sees them
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+
+    if (!has_chunk)
+        return;
     const int64_t rec = ((int64_t)t * a.C + k) * a.H;
-    if (mask == 0) {                // empty chunk: (-inf, +0), o left alone
+    if (!work) {                     // empty chunk: (-inf, +0), o left alone
         if (lane < a.H) {
             a.m[rec + lane] = -INFINITY;
             a.l[rec + lane] = 0.0f;
@@ -158,20 +228,23 @@ __global__ __launch_bounds__(64 * kWaves) void attn_kernel(AttnArgs a)
         return;
     }
 
-    // ---- per-cell scales (zero for empty slots); K scales carry the softmax scale
-    uint2 ks = make_uint2(0u, 0u), vs = make_uint2(0u, 0u);
-    if (valid) {
-        ks = *(const uint2 *)(a.ksc + (int64_t)sid * 4);
-        vs = *(const uint2 *)(a.vsc + (int64_t)sid * 4);
+    // ---- scales: V scales may need a common power-of-two factor so that
+    // vq * vsc stays inside fp16 range ----------------------------------------
+    uint32_t ev = max(max((vs.x >> 10) & 31u, (vs.x >> 26) & 31u),
+                      max((vs.y >> 10) & 31u, (vs.y >> 26) & 31u));
+    uint32_t e = 0;                 // largest biased exponent in the chunk, bit by bit
+#pragma unroll
+    for (int bit = 4; bit >= 0; --bit) {
+        const uint32_t c = e | (1u << bit);
+        if (__ballot(ev >= c) != 0)
+            e = c;
     }
-    // largest biased fp16 exponent among the chunk's V scales
-    uint32_t e = max(max((vs.x >> 10) & 31u, (vs.x >> 26) & 31u),
-                     max((vs.y >> 10) & 31u, (vs.y >> 26) & 31u));
-    e = wave_max_u32(e);
-    const float up = __int_as_float((127 + 15 - (int)e) << 23);     // 2^(15 - e)
+    // |vq| <= 127 and vsc < 2^(e - 14): no overflow below vsc = 2^9
+    const bool renorm = e >= 24;
     const float down = __int_as_float((127 - 15 + (int)e) << 23);   // 2^(e - 15)
-    uint2 vn;
-    {
+    uint2 vn = vs;
+    if (renorm) {
+        const float up = __int_as_float((127 + 15 - (int)e) << 23); // 2^(15 - e)
         _Float16 h0 = (_Float16)(half_bits_to_float(vs.x & 0xffffu) * up);
         _Float16 h1 = (_Float16)(half_bits_to_float(vs.x >> 16) * up);
         _Float16 h2 = (_Float16)(half_bits_to_float(vs.y & 0xffffu) * up);
@@ -179,62 +252,40 @@ __global__ __launch_bounds__(64 * kWaves) void attn_kernel(AttnArgs a)
         vn.x = (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
         vn.y = (uint32_t)__builtin_bit_cast(uint16_t, h2) | ((uint32_t)__builtin_bit_cast(uint16_t, h3) << 16);
     }
-    s_ksc[w][lane] = make_float4(a.scale * half_bits_to_float(ks.x & 0xffffu), a.scale * half_bits_to_float(ks.x >> 16),
-                                 a.scale * half_bits_to_float(ks.y & 0xffffu), a.scale * half_bits_to_float(ks.y >> 16));
-    s_vsc[w][0][lane] = (uint16_t)(vn.x & 0xffffu);
-    s_vsc[w][1][lane] = (uint16_t)(vn.x >> 16);
-    s_vsc[w][2][lane] = (uint16_t)(vn.y & 0xffffu);
-    s_vsc[w][3][lane] = (uint16_t)(vn.y >> 16);
-    s_id[w][lane] = sid;
+    s_ksc[lane] = ks;
+    s_vsc[0 * kChunk + lane] = (uint16_t)(vn.x & 0xffffu);
+    s_vsc[1 * kChunk + lane] = (uint16_t)(vn.x >> 16);
+    s_vsc[2 * kChunk + lane] = (uint16_t)(vn.y & 0xffffu);
+    s_vsc[3 * kChunk + lane] = (uint16_t)(vn.y >> 16);
     wave_sync_lds();
 
-    // ---- gathers: K rows (A operand of QK), V rows (B operand of PV), q -----
-    // K: lane (j, c16) of block b holds cell 16b + c16, dims 32g + 8j .. +7.
-    uint2 kraw[4][4];
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-        const uint32_t kr = (uint32_t)s_id[w][16 * b + c16] * kD + 8 * j;   // n_cells * 128 < 2^32
-#pragma unroll
-        for (int g = 0; g < 4; ++g)
-            kraw[b][g] = *(const uint2 *)(a.kq + (kr + 32 * g));
-    }
-    // V: slot s of k-step ks is cell 32ks + 16(s/4) + 4j + s%4 -- the cells whose
-    // scores this lane holds -- and the lane reads dims 8*c16 .. 8*c16+7.
-    uint2 vraw[2][8];
-#pragma unroll
-    for (int ks2 = 0; ks2 < 2; ++ks2)
-#pragma unroll
-        for (int s = 0; s < 8; ++s) {
-            const int cell = 32 * ks2 + 16 * (s >> 2) + 4 * j + (s & 3);
-            vraw[ks2][s] = *(const uint2 *)(a.vq + ((uint32_t)s_id[w][cell] * kD + 8 * c16));
-        }
-    // q: head c16, dims 32g + 8j .. +7 (zero for padding heads)
+    // q operand: head c16, dims 32g + 8j .. +7 (zero for padding heads)
     half8 qop[4];
-    if (c16 < a.H) {
-        const half8 *qr = (const half8 *)(a.q + ((int64_t)t * a.H + c16) * kD + 8 * j);
 #pragma unroll
-        for (int g = 0; g < 4; ++g)
-            qop[g] = qr[4 * g];
-    } else {
-#pragma unroll
-        for (int g = 0; g < 4; ++g)
-            qop[g] = (half8)(_Float16)0.0f;
-    }
+    for (int g = 0; g < 4; ++g)
+        qop[g] = c16 < a.H ? *(const half8 *)(qrows + qrow_offset(c16, 4 * g + j)) : (half8)(_Float16)0.0f;
 
     // ---- scores: S[b][r] is cell 16b + 4j + r, head c16 ----------------------
     float S[4][4];
     const floatx4 zero = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
+        // A operand: cell 16b + c16, dims 32g + 8j .. +7 = bytes 16(2g + j/2) + 8(j&1)
         floatx4 acc[4];
+        const int row = 16 * b + c16;
 #pragma unroll
-        for (int g = 0; g < 4; ++g)
-            acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(i8x8_to_half8(kraw[b][g]), qop[g], zero, 0, 0, 0);
+        for (int g = 0; g < 4; ++g) {
+            const uint2 kr = *(const uint2 *)(ktile + ktile_offset(row, 2 * g + (j >> 1)) + 8 * (j & 1));
+            acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(i8x8_to_half8(kr), qop[g], zero, 0, 0, 0);
+        }
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int cell = 16 * b + 4 * j + r;
-            const float4 kb = s_ksc[w][cell];
-            const float sv = (acc[0][r] * kb.x + acc[1][r] * kb.y) + (acc[2][r] * kb.z + acc[3][r] * kb.w);
+            const uint2 kb = s_ksc[cell];
+            const float sv = a.scale * ((acc[0][r] * half_bits_to_float(kb.x & 0xffffu) +
+                                         acc[1][r] * half_bits_to_float(kb.x >> 16)) +
+                                        (acc[2][r] * half_bits_to_float(kb.y & 0xffffu) +
+                                         acc[3][r] * half_bits_to_float(kb.y >> 16)));
             S[b][r] = ((mask >> cell) & 1ull) ? sv : -INFINITY;
         }
     }
@@ -282,7 +333,7 @@ __global__ __launch_bounds__(64 * kWaves) void attn_kernel(AttnArgs a)
 #pragma unroll
         for (int sp = 0; sp < 4; ++sp) {
             const int cell = 32 * ks2 + 16 * (sp >> 1) + 4 * j + 2 * (sp & 1);
-            sc[sp] = __builtin_bit_cast(half2v, *(const uint32_t *)&s_vsc[w][c16 >> 2][cell]);
+            sc[sp] = __builtin_bit_cast(half2v, *(const uint32_t *)&s_vsc[(c16 >> 2) * kChunk + cell]);
         }
 #pragma unroll
         for (int tt = 0; tt < 8; ++tt) {
@@ -306,15 +357,18 @@ __global__ __launch_bounds__(64 * kWaves) void attn_kernel(AttnArgs a)
     }
 
     // ---- write the chunk record ----------------------------------------------
+    if (renorm) {                   // take the V scales' power of two back out, exactly
+#pragma unroll
+        for (int tt = 0; tt < 8; ++tt)
+            O[tt] *= down;
+    }
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
         const int head = 4 * j + r;
         if (head < a.H) {
             float *dst = a.o + (rec + head) * kD + 8 * c16;
-            float4 v0 = make_float4(O[0][r] * down, O[1][r] * down, O[2][r] * down, O[3][r] * down);
-            float4 v1 = make_float4(O[4][r] * down, O[5][r] * down, O[6][r] * down, O[7][r] * down);
-            *(float4 *)dst = v0;
-            *(float4 *)(dst + 4) = v1;
+            *(float4 *)dst = make_float4(O[0][r], O[1][r], O[2][r], O[3][r]);
+            *(float4 *)(dst + 4) = make_float4(O[4][r], O[5][r], O[6][r], O[7][r]);
         }
     }
     if (j == 0 && c16 < a.H) {
@@ -328,7 +382,7 @@ __global__ __launch_bounds__(64 * kWaves) void attn_kernel(AttnArgs a)
 hipError_t launch_attn(const AttnArgs &a, hipStream_t stream)
 {
     dim3 grid(8 * a.blocks_per_xcd), block(64 * kWaves);
-    hipLaunchKernelGGL(attn_kernel, grid, block, 0, stream, a);
+    hipLaunchKernelGGL(attn_kernel, grid, block, attn_lds_bytes(a.H), stream, a);
     return hipGetLastError();
 }
 
