@@ -10,16 +10,20 @@
 // skipped without reading their o, which qsa_attn leaves unwritten.
 //
 // The merge streams the partial records once, so it is bound by HBM reads.
-// One 64-lane wave owns one (token, head) pair. The lanes first reduce the
-// chunk maxima; then the wave walks the chunks in order, eight at a time, with
-// each lane owning two dims, so every record row is one coalesced 512-byte read
-// and eight of them are in flight per wave. The walk has no branches: records
-// of empty chunks (or past the end) are still addressed, but their products are
-// discarded by a select, so a stale o never reaches the sums.
+// Each half of a 64-lane wave owns one (token, head) pair, so a wave covers two
+// adjacent 512-byte head rows of a chunk record with one 16-byte load per lane.
+// The lanes first reduce the chunk maxima; then the wave walks the chunks in
+// order, eight at a time, so eight such loads are in flight. The records are
+// read once and never again, so the loads are marked nontemporal. The walk has
+// no branches: records of empty chunks (or past the end) are still addressed,
+// but their products are discarded by a select, so a stale o never reaches the
+// sums.
 #include "qsa_internal.h"
 
 namespace qsa {
 namespace {
+
+typedef float f4v __attribute__((ext_vector_type(4)));
 
 constexpr int kWaves = 4;
 constexpr float kLog2e = 1.4426950408889634f;
@@ -28,58 +32,65 @@ __global__ __launch_bounds__(64 * kWaves) void merge_kernel(MergeArgs a)
 {
     constexpr int kUnroll = 8;
     const int lane = threadIdx.x & 63;
-    const int64_t wv = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
-    if (wv >= (int64_t)a.T * a.H)
-        return;
-    const int t = (int)(wv / a.H);
-    const int h = (int)(wv - (int64_t)t * a.H);
-    const int64_t base = (int64_t)t * a.C * a.H + h;     // record (t, 0, h); chunk stride H
+    const int half = lane >> 5, l32 = lane & 31;
+    const int64_t hv = ((int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6)) * 2 + half;   // (t, h) pair
+    const bool live = hv < (int64_t)a.T * a.H;
+    const int64_t hv2 = live ? hv : 0;
+    const int t = (int)(hv2 / a.H);
+    const int h = (int)(hv2 - (int64_t)t * a.H);
+    const int64_t base = (int64_t)t * a.C * a.H + h;
 
     float M = -INFINITY;
-    for (int k0 = 0; k0 < a.C; k0 += 64) {
-        const int k = k0 + lane;
+    for (int k0 = 0; k0 < a.C; k0 += 32) {
+        const int k = k0 + l32;
         if (k < a.C)
             M = fmaxf(M, a.m[base + (int64_t)k * a.H]);
     }
 #pragma unroll
-    for (int s = 32; s >= 1; s >>= 1)
+    for (int s = 16; s >= 1; s >>= 1)
         M = fmaxf(M, __shfl_xor(M, s, 64));
 
-    uint32_t res = 0u;              // two fp16 +0 values
+    uint2 res = make_uint2(0u, 0u);
     if (M != -INFINITY) {
-        float L = 0.0f, O0 = 0.0f, O1 = 0.0f;
+        float L = 0.0f;
+        float4 O = make_float4(0.f, 0.f, 0.f, 0.f);
         for (int k0 = 0; k0 < a.C; k0 += kUnroll) {
             float mk[kUnroll], lk[kUnroll];
-            float2 ov[kUnroll];
+            float4 ov[kUnroll];
 #pragma unroll
             for (int u = 0; u < kUnroll; ++u) {
                 const int k = min(k0 + u, a.C - 1);
                 const int64_t r = base + (int64_t)k * a.H;
                 mk[u] = a.m[r];
                 lk[u] = a.l[r];
-                ov[u] = *(const float2 *)(a.o + r * kD + 2 * lane);
+                { f4v t4 = __builtin_nontemporal_load((const f4v *)(a.o + r * kD + 4 * l32)); ov[u] = make_float4(t4.x, t4.y, t4.z, t4.w); }
             }
 #pragma unroll
             for (int u = 0; u < kUnroll; ++u) {
                 const bool use = (k0 + u < a.C) && (mk[u] != -INFINITY);
                 const float wk = __builtin_amdgcn_exp2f((mk[u] - M) * kLog2e);
                 L = use ? fmaf(wk, lk[u], L) : L;
-                O0 = use ? fmaf(wk, ov[u].x, O0) : O0;
-                O1 = use ? fmaf(wk, ov[u].y, O1) : O1;
+                O.x = use ? fmaf(wk, ov[u].x, O.x) : O.x;
+                O.y = use ? fmaf(wk, ov[u].y, O.y) : O.y;
+                O.z = use ? fmaf(wk, ov[u].z, O.z) : O.z;
+                O.w = use ? fmaf(wk, ov[u].w, O.w) : O.w;
             }
         }
-        const _Float16 r0 = (_Float16)(O0 / L);
-        const _Float16 r1 = (_Float16)(O1 / L);
-        res = (uint32_t)__builtin_bit_cast(uint16_t, r0) | ((uint32_t)__builtin_bit_cast(uint16_t, r1) << 16);
+        const _Float16 r0 = (_Float16)(O.x / L), r1 = (_Float16)(O.y / L);
+        const _Float16 r2 = (_Float16)(O.z / L), r3 = (_Float16)(O.w / L);
+        res.x = (uint32_t)__builtin_bit_cast(uint16_t, r0) | ((uint32_t)__builtin_bit_cast(uint16_t, r1) << 16);
+        res.y = (uint32_t)__builtin_bit_cast(uint16_t, r2) | ((uint32_t)__builtin_bit_cast(uint16_t, r3) << 16);
     }
-    *(uint32_t *)(a.out + ((int64_t)t * a.H + h) * kD + 2 * lane) = res;
+    if (live)
+        *(uint2 *)(a.out + ((int64_t)t * a.H + h) * kD + 4 * l32) = res;
 }
 
 } // namespace
 
 hipError_t launch_merge(const MergeArgs &a, hipStream_t stream)
 {
-    const int64_t waves = (int64_t)a.T * a.H;
+    const int64_t pairs = (int64_t)a.T * a.H;
+    const int64_t waves = (pairs + 1) / 2;
     dim3 grid((unsigned)((waves + kWaves - 1) / kWaves)), block(64 * kWaves);
     hipLaunchKernelGGL(merge_kernel, grid, block, 0, stream, a);
     return hipGetLastError();
