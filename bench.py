@@ -240,12 +240,14 @@ def main():
 
     if args.copy_calibration:
         # one elementwise kernel that reads n bytes and writes n bytes
-        # (its input is pushed out of L2 and the Infinity Cache first by a larger fill)
+        # (its input is first pushed out of L2 and the Infinity Cache by reading a
+        # larger buffer, so no dirty lines are written back while the copy runs)
         n = args.copy_calibration << 20
+        flush = torch.full((3 * n // 4,), 2.0, dtype=torch.float32, device=dev)
         a = torch.ones(n // 4, dtype=torch.float32, device=dev)
         b = torch.empty_like(a)
-        flush = torch.empty(3 * n // 4, dtype=torch.float32, device=dev)
-        flush.fill_(2.0)
+        torch.cuda.synchronize()
+        flush.sum()
         torch.cuda.synchronize()
         torch.mul(a, 1.0, out=b)
         torch.cuda.synchronize()
