@@ -105,6 +105,7 @@ def main():
     ap.add_argument("--cpu-tokens", type=int, default=384)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
     ap.add_argument("--no-score", action="store_true", help="skip the companion score kernel")
+    ap.add_argument("--no-fused", action="store_true", help="skip the single-dispatch attention + merge line")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="also run one device copy of this many MiB (for counter calibration)")
     args = ap.parse_args()
@@ -214,6 +215,32 @@ def main():
             "traffic": traffic,
         },
     }
+
+    if not args.no_fused:
+        # attention and merge in one dispatch (no chunk records in memory)
+        fout = [torch.empty(T, H, D, dtype=torch.float16, device=dev) for _ in range(args.layers)]
+        for _ in range(2):
+            for li, (q, kq, vq, ksc, vsc) in enumerate(layers):
+                qsa.qsa_attn_merge(q, kq, vq, ksc, vsc, ids, case.pos0, scale, fout[li], stream=stream)
+        torch.cuda.synchronize()
+        fev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+        for s in range(args.steps):
+            fev[s][0].record(stream)
+            for li, (q, kq, vq, ksc, vsc) in enumerate(layers):
+                qsa.qsa_attn_merge(q, kq, vq, ksc, vsc, ids, case.pos0, scale, fout[li], stream=stream)
+            fev[s][1].record(stream)
+        torch.cuda.synchronize()
+        f_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in fev]))
+        fdiff = float((fout[0].float() - outs[0].float()).abs().max())
+        result["fused_path"] = {
+            "entry": "qsa_attn_merge",
+            "value": T * H * args.layers / (f_ms * 1e-3),
+            "unit": "query-token*heads/s",
+            "ms_per_step": f_ms,
+            "avg_us_per_launch": f_ms * 1e3 / args.layers,
+            "max_abs_diff_vs_two_kernel_path": fdiff,
+        }
+        del fout
 
     if not args.no_score:
         sc = synth.score_case(T=T, pos0=case.pos0, Hs=12)

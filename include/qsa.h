@@ -95,6 +95,26 @@ QSA_API qsa_status qsa_attn(const void *q, const int8_t *kq, const int8_t *vq,
                     float scale, void *part, void *stream);
 
 /*
+ * qsa_attn_merge -- explicit-selection attention and the merge of its chunk
+ * records in one dispatch, with no partial records written to memory.
+ *
+ * Defined by "round 5 track b: cached residual norms and fused mtp attention",
+ * section "mtp attention" (a decode kernel that keeps every chunk's
+ * probabilities, maxima and denominators on chip and merges them before it
+ * writes the output), applied here to any number of tokens and chunks.
+ *
+ * out[t][h][d] is the value qsa_attn followed by qsa_merge computes, up to
+ * rounding: the chunk records are combined relative to the running largest
+ * chunk maximum as they are produced. Arguments are those of qsa_attn, with
+ *   out      fp16 [T][H][D], 16-byte aligned, in place of `part`.
+ */
+QSA_API qsa_status qsa_attn_merge(const void *q, const int8_t *kq, const int8_t *vq,
+                          const void *ksc, const void *vsc, int32_t n_cells,
+                          const int32_t *ids, int32_t ids_stride,
+                          int32_t pos0, int32_t T, int32_t H, int32_t D,
+                          float scale, void *out, void *stream);
+
+/*
  * qsa_merge -- max-first merge of chunk records into fp16 output.
  *
  * Defined by "round 5 track b: cached residual norms and fused mtp attention",

@@ -16,7 +16,7 @@ import torch
 
 __all__ = [
     "QsaError", "CHUNK", "GROUP", "HEAD_DIM",
-    "qsa_attn", "qsa_merge", "qsa_score", "qsa_part_bytes", "qsa_part_offsets", "qsa_last_error",
+    "qsa_attn", "qsa_attn_merge", "qsa_merge", "qsa_score", "qsa_part_bytes", "qsa_part_offsets", "qsa_last_error",
     "alloc_part", "part_views", "chunk_count", "lib", "LIB_PATH",
 ]
 
@@ -48,6 +48,8 @@ def lib() -> ctypes.CDLL:
         P, i32, i64, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float
         L.qsa_attn.argtypes = [P, P, P, P, P, i32, P, i32, i32, i32, i32, i32, f32, P, P]
         L.qsa_attn.restype = ctypes.c_int
+        L.qsa_attn_merge.argtypes = [P, P, P, P, P, i32, P, i32, i32, i32, i32, i32, f32, P, P]
+        L.qsa_attn_merge.restype = ctypes.c_int
         L.qsa_merge.argtypes = [P, i32, i32, i32, i32, P, P]
         L.qsa_merge.restype = ctypes.c_int
         L.qsa_score.argtypes = [P, P, i32, i32, i32, i32, i32, f32, f32, P, i64, P]
@@ -127,15 +129,7 @@ def _need(t: torch.Tensor, name: str, dtype: torch.dtype, ndim: int):
         raise ValueError("%s must be contiguous" % name)
 
 
-def qsa_attn(q: torch.Tensor, kq: torch.Tensor, vq: torch.Tensor, ksc: torch.Tensor, vsc: torch.Tensor,
-             ids: Optional[torch.Tensor], pos0: int, scale: float, part: torch.Tensor,
-             stream=None) -> int:
-    """Chunk records of explicit-selection attention; returns the chunk count C.
-
-    q fp16 [T][H][D]; kq, vq int8 [n_cells][D]; ksc, vsc fp16 [n_cells][D/32];
-    ids int32 [T][64*C] with -1 poison, or None for implicit all-causal rows;
-    part: a byte tensor of at least qsa_part_bytes(T, H, D, C) bytes.
-    """
+def _check_attn_inputs(q, kq, vq, ksc, vsc, ids):
     _need(q, "q", torch.float16, 3)
     T, H, D = q.shape
     _need(kq, "kq", torch.int8, 2)
@@ -153,6 +147,30 @@ def qsa_attn(q: torch.Tensor, kq: torch.Tensor, vq: torch.Tensor, ksc: torch.Ten
         if ids.shape[0] != T:
             raise ValueError("ids must have T rows")
         stride = ids.shape[1]
+    return T, H, D, n_cells, stride
+
+
+def qsa_attn_merge(q: torch.Tensor, kq: torch.Tensor, vq: torch.Tensor, ksc: torch.Tensor, vsc: torch.Tensor,
+                   ids: Optional[torch.Tensor], pos0: int, scale: float, out: torch.Tensor, stream=None) -> None:
+    """Attention and the merge in one dispatch: fp16 out [T][H][D], no chunk records."""
+    T, H, D, n_cells, stride = _check_attn_inputs(q, kq, vq, ksc, vsc, ids)
+    _need(out, "out", torch.float16, 3)
+    if tuple(out.shape) != (T, H, D):
+        raise ValueError("out must be [T][H][D]")
+    _raise_on(lib().qsa_attn_merge(_ptr(q), _ptr(kq), _ptr(vq), _ptr(ksc), _ptr(vsc), n_cells, _ptr(ids), stride,
+                                   pos0, T, H, D, float(scale), _ptr(out), _stream(stream)))
+
+
+def qsa_attn(q: torch.Tensor, kq: torch.Tensor, vq: torch.Tensor, ksc: torch.Tensor, vsc: torch.Tensor,
+             ids: Optional[torch.Tensor], pos0: int, scale: float, part: torch.Tensor,
+             stream=None) -> int:
+    """Chunk records of explicit-selection attention; returns the chunk count C.
+
+    q fp16 [T][H][D]; kq, vq int8 [n_cells][D]; ksc, vsc fp16 [n_cells][D/32];
+    ids int32 [T][64*C] with -1 poison, or None for implicit all-causal rows;
+    part: a byte tensor of at least qsa_part_bytes(T, H, D, C) bytes.
+    """
+    T, H, D, n_cells, stride = _check_attn_inputs(q, kq, vq, ksc, vsc, ids)
     C = chunk_count(ids, pos0, T)
     if part.device.type != "cuda" or not part.is_contiguous():
         raise ValueError("part must be a contiguous device tensor")

@@ -96,48 +96,45 @@ void qsa_part_offsets(int32_t T, int32_t H, int32_t D, int32_t n_chunks,
 
 const char *qsa_last_error(void) { return g_err; }
 
-qsa_status qsa_attn(const void *q, const int8_t *kq, const int8_t *vq,
-                    const void *ksc, const void *vsc, int32_t n_cells,
-                    const int32_t *ids, int32_t ids_stride,
-                    int32_t pos0, int32_t T, int32_t H, int32_t D,
-                    float scale, void *part, void *stream)
-{
-    if (T < 0 || pos0 < 0 || n_cells < 0)
-        return fail(QSA_ERR_ARG, "qsa_attn: negative T (%d), pos0 (%d) or n_cells (%d)", T, pos0, n_cells);
-    if (H < 1)
-        return fail(QSA_ERR_ARG, "qsa_attn: H must be >= 1 (got %d)", H);
-    if (H > qsa::kMaxHeads)
-        return fail(QSA_ERR_UNSUPPORTED, "qsa_attn: at most %d heads (got %d)", qsa::kMaxHeads, H);
-    if (D != qsa::kD)
-        return fail(QSA_ERR_UNSUPPORTED, "qsa_attn: head dim %d not implemented (only %d)", D, qsa::kD);
-    if (ids && (ids_stride <= 0 || ids_stride % QSA_CHUNK != 0))
-        return fail(QSA_ERR_ARG, "qsa_attn: ids_stride must be a positive multiple of %d (got %d)",
-                    QSA_CHUNK, ids_stride);
-    if ((int64_t)pos0 + T > INT32_MAX)
-        return fail(QSA_ERR_ARG, "qsa_attn: pos0 + T overflows int32");
-    if (n_cells > qsa::kMaxCells)
-        return fail(QSA_ERR_UNSUPPORTED, "qsa_attn: at most %d cached rows (got %d)", qsa::kMaxCells, n_cells);
-    if (T == 0)
-        return ok();
-    if (!q || !kq || !vq || !ksc || !vsc || !part)
-        return fail(QSA_ERR_ARG, "qsa_attn: NULL q, kq, vq, ksc, vsc or part");
-    if (!aligned(q, 16) || !aligned(kq, 16) || !aligned(vq, 16) || !aligned(ksc, 8) ||
-        !aligned(vsc, 8) || !aligned(part, 256) || (ids && !aligned(ids, 4)))
-        return fail(QSA_ERR_ARG, "qsa_attn: misaligned pointer (q, kq, vq: 16 B; ksc, vsc: 8 B; "
-                                 "part: 256 B; ids: 4 B)");
-    const int64_t C = ids ? ids_stride / QSA_CHUNK : ((int64_t)pos0 + T + QSA_CHUNK - 1) / QSA_CHUNK;
-    const int64_t n_blocks = (C + qsa::kAttnWaves - 1) / qsa::kAttnWaves * T;   // (chunk group, token)
-    const int64_t per_xcd = (n_blocks + 7) / 8;
-    if (C > INT32_MAX || per_xcd * 8 > INT32_MAX)
-        return fail(QSA_ERR_ARG, "qsa_attn: T * chunks too large for one launch");
-    qsa_status st = check_device();
-    if (st != QSA_OK)
-        return st;
+} // extern "C"
 
-    size_t o_off, m_off, l_off;
-    qsa::part_layout(T, H, D, C, &o_off, &m_off, &l_off, nullptr);
-    char *pb = static_cast<char *>(part);
-    qsa::AttnArgs a;
+namespace {
+
+// Checks shared by qsa_attn and qsa_attn_merge; fills the geometry of `a`.
+// Returns QSA_OK with *noop set when T == 0.
+qsa_status check_attn(const char *fn, const void *q, const int8_t *kq, const int8_t *vq, const void *ksc,
+                      const void *vsc, int32_t n_cells, const int32_t *ids, int32_t ids_stride, int32_t pos0,
+                      int32_t T, int32_t H, int32_t D, float scale, qsa::AttnArgs &a, bool *noop)
+{
+    *noop = false;
+    if (T < 0 || pos0 < 0 || n_cells < 0)
+        return fail(QSA_ERR_ARG, "%s: negative T (%d), pos0 (%d) or n_cells (%d)", fn, T, pos0, n_cells);
+    if (H < 1)
+        return fail(QSA_ERR_ARG, "%s: H must be >= 1 (got %d)", fn, H);
+    if (H > qsa::kMaxHeads)
+        return fail(QSA_ERR_UNSUPPORTED, "%s: at most %d heads (got %d)", fn, qsa::kMaxHeads, H);
+    if (D != qsa::kD)
+        return fail(QSA_ERR_UNSUPPORTED, "%s: head dim %d not implemented (only %d)", fn, D, qsa::kD);
+    if (ids && (ids_stride <= 0 || ids_stride % QSA_CHUNK != 0))
+        return fail(QSA_ERR_ARG, "%s: ids_stride must be a positive multiple of %d (got %d)", fn, QSA_CHUNK,
+                    ids_stride);
+    if ((int64_t)pos0 + T > INT32_MAX)
+        return fail(QSA_ERR_ARG, "%s: pos0 + T overflows int32", fn);
+    if (n_cells > qsa::kMaxCells)
+        return fail(QSA_ERR_UNSUPPORTED, "%s: at most %d cached rows (got %d)", fn, qsa::kMaxCells, n_cells);
+    if (T == 0) {
+        *noop = true;
+        return QSA_OK;
+    }
+    if (!q || !kq || !vq || !ksc || !vsc)
+        return fail(QSA_ERR_ARG, "%s: NULL q, kq, vq, ksc or vsc", fn);
+    if (!aligned(q, 16) || !aligned(kq, 16) || !aligned(vq, 16) || !aligned(ksc, 8) || !aligned(vsc, 8) ||
+        (ids && !aligned(ids, 4)))
+        return fail(QSA_ERR_ARG, "%s: misaligned pointer (q, kq, vq: 16 B; ksc, vsc: 8 B; ids: 4 B)", fn);
+    const int64_t C = ids ? ids_stride / QSA_CHUNK : ((int64_t)pos0 + T + QSA_CHUNK - 1) / QSA_CHUNK;
+    if (C > INT32_MAX)
+        return fail(QSA_ERR_ARG, "%s: too many chunks", fn);
+    a = qsa::AttnArgs{};
     a.q = static_cast<const _Float16 *>(q);
     a.kq = kq;
     a.vq = vq;
@@ -151,12 +148,74 @@ qsa_status qsa_attn(const void *q, const int8_t *kq, const int8_t *vq,
     a.H = H;
     a.C = (int32_t)C;
     a.scale = scale;
+    return QSA_OK;
+}
+
+} // namespace
+
+extern "C" {
+
+qsa_status qsa_attn(const void *q, const int8_t *kq, const int8_t *vq,
+                    const void *ksc, const void *vsc, int32_t n_cells,
+                    const int32_t *ids, int32_t ids_stride,
+                    int32_t pos0, int32_t T, int32_t H, int32_t D,
+                    float scale, void *part, void *stream)
+{
+    qsa::AttnArgs a;
+    bool noop;
+    qsa_status st = check_attn("qsa_attn", q, kq, vq, ksc, vsc, n_cells, ids, ids_stride, pos0, T, H, D, scale,
+                               a, &noop);
+    if (st != QSA_OK)
+        return st;
+    if (noop)
+        return ok();
+    if (!part)
+        return fail(QSA_ERR_ARG, "qsa_attn: NULL part");
+    if (!aligned(part, 256))
+        return fail(QSA_ERR_ARG, "qsa_attn: misaligned part (256 B)");
+    const int64_t n_blocks = ((int64_t)a.C + qsa::kAttnWaves - 1) / qsa::kAttnWaves * T;   // (chunk group, token)
+    const int64_t per_xcd = (n_blocks + 7) / 8;
+    if (per_xcd * 8 > INT32_MAX)
+        return fail(QSA_ERR_ARG, "qsa_attn: T * chunks too large for one launch");
+    st = check_device();
+    if (st != QSA_OK)
+        return st;
+    size_t o_off, m_off, l_off;
+    qsa::part_layout(T, H, D, a.C, &o_off, &m_off, &l_off, nullptr);
+    char *pb = static_cast<char *>(part);
     a.o = reinterpret_cast<float *>(pb + o_off);
     a.m = reinterpret_cast<float *>(pb + m_off);
     a.l = reinterpret_cast<float *>(pb + l_off);
     a.n_blocks = (int32_t)n_blocks;
     a.blocks_per_xcd = (int32_t)per_xcd;
     return launched(qsa::launch_attn(a, static_cast<hipStream_t>(stream)), "qsa_attn");
+}
+
+qsa_status qsa_attn_merge(const void *q, const int8_t *kq, const int8_t *vq,
+                          const void *ksc, const void *vsc, int32_t n_cells,
+                          const int32_t *ids, int32_t ids_stride,
+                          int32_t pos0, int32_t T, int32_t H, int32_t D,
+                          float scale, void *out, void *stream)
+{
+    qsa::AttnArgs a;
+    bool noop;
+    qsa_status st = check_attn("qsa_attn_merge", q, kq, vq, ksc, vsc, n_cells, ids, ids_stride, pos0, T, H, D,
+                               scale, a, &noop);
+    if (st != QSA_OK)
+        return st;
+    if (noop)
+        return ok();
+    if (!out)
+        return fail(QSA_ERR_ARG, "qsa_attn_merge: NULL out");
+    if (!aligned(out, 16))
+        return fail(QSA_ERR_ARG, "qsa_attn_merge: misaligned out (16 B)");
+    st = check_device();
+    if (st != QSA_OK)
+        return st;
+    a.out = static_cast<_Float16 *>(out);
+    a.n_blocks = T;
+    a.blocks_per_xcd = (T + 7) / 8;
+    return launched(qsa::launch_attn_merge(a, static_cast<hipStream_t>(stream)), "qsa_attn_merge");
 }
 
 qsa_status qsa_merge(const void *part, int32_t n_chunks, int32_t T, int32_t H, int32_t D,

@@ -62,7 +62,7 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kKTileBytes = kChunk * kD;                 // 8 KB of K rows per wave
 constexpr int kWaveBytes = kKTileBytes + kChunk * 8      // K tile, K scales (fp16 x 4)
                            + kChunk * 8 + kChunk * 4;    // V scales (group-major), cell ids
-constexpr int attn_lds_bytes(int H) { return kWaves * kWaveBytes + H * kD * 2; }
+constexpr int attn_lds_bytes(int nw, int H) { return nw * kWaveBytes + H * kD * 2; }
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -133,63 +133,67 @@ __device__ inline int ktile_offset(int row, int lg) { return row * kD + ((lg ^ (
 // q rows: head h holds 16 granules; logical granule lg sits at lg ^ (h & 15).
 __device__ inline int qrow_offset(int h, int lg) { return h * (kD * 2) + ((lg ^ (h & 15)) << 4); }
 
-__global__ __launch_bounds__(64 * kWaves) void attn_kernel(AttnArgs a)
+// ---- per-wave LDS regions ----------------------------------------------------
+
+struct WaveLds {
+    uint8_t *ktile;      // [64 rows][128 B], swizzled granules
+    uint2 *ksc;          // [64] cells x 4 fp16 K scales
+    uint16_t *vsc;       // [4 groups][64 cells] fp16 V scales
+    int32_t *id;         // [64] cell ids (0 for empty slots)
+};
+
+__device__ inline WaveLds wave_lds(uint8_t *lds, int w)
 {
-    extern __shared__ __align__(16) uint8_t lds[];
+    uint8_t *base = lds + w * kWaveBytes;
+    return WaveLds{base, (uint2 *)(base + kKTileBytes), (uint16_t *)(base + kKTileBytes + kChunk * 8),
+                   (int32_t *)(base + kKTileBytes + kChunk * 16)};
+}
 
-    const int lane = threadIdx.x & 63;
-    const int w = threadIdx.x >> 6;
-    const int j = lane >> 4;        // 16-lane row of the wave
-    const int c16 = lane & 15;      // column inside a 16-wide MFMA tile
-
-    // each XCD (workgroup id mod 8) walks a contiguous range of workgroups
-    const int lb = (blockIdx.x & 7) * a.blocks_per_xcd + (blockIdx.x >> 3);
-    if (lb >= a.n_blocks)
-        return;                     // uniform over the workgroup
-    const int kg = lb / a.T;
-    const int t = lb - kg * a.T;
-    const int k = kWaves * kg + w;
-    const bool has_chunk = k < a.C;
-    const int p = a.pos0 + t;
-
-    uint8_t *ktile = lds + w * kWaveBytes;
-    uint2 *s_ksc = (uint2 *)(ktile + kKTileBytes);                      // [64] x 4 fp16
-    uint16_t *s_vsc = (uint16_t *)(ktile + kKTileBytes + kChunk * 8);   // [4][64] fp16
-    int32_t *s_id = (int32_t *)(ktile + kKTileBytes + kChunk * 16);     // [64]
-    uint8_t *qrows = lds + kWaves * kWaveBytes;                         // [H][256 B]
-
-    // ---- the token's q rows into LDS, once for the workgroup ---------------
-    // wave w copies granules 64w .. 64w+63 of the H rows of 16 granules
-    {
-        const int gi = 64 * w + lane;            // destination granule
+// The token's q rows (H x 256 B) into LDS: 16-byte granules, head h's logical
+// granule lg at lg ^ (h & 15). Waves 0..nw-1 share the copy, 1 KB per load.
+__device__ inline void copy_q_rows(const AttnArgs &a, uint8_t *qrows, int t, int w, int nw, int lane)
+{
+    for (int g0 = 64 * w; g0 < 16 * a.H; g0 += 64 * nw) {
+        const int gi = g0 + lane;                // destination granule
         const int h = gi >> 4, phys = gi & 15;
         if (h < a.H) {
             const int lg = phys ^ (h & 15);
             const _Float16 *src = a.q + ((int64_t)t * a.H + h) * kD + 8 * lg;
-            __builtin_amdgcn_global_load_lds((const void *)src, (lds_void *)(qrows + 1024 * w), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds((const void *)src, (lds_void *)(qrows + 16 * g0), 16, 0, 0);
         }
     }
+}
 
-    // ---- ids and the valid mask --------------------------------------------
-    int32_t id = -1;
-    if (has_chunk) {
-        const int64_t slot = (int64_t)k * kChunk + lane;
-        if (a.ids)
-            id = a.ids[(int64_t)t * a.ids_stride + slot];
-        else
-            id = slot <= p ? (int32_t)slot : -1;
-    }
+// q operand of QK: head c16, dims 32g + 8j .. +7 (zero for padding heads)
+__device__ inline void q_operand(const AttnArgs &a, const uint8_t *qrows, int j, int c16, half8 (&qop)[4])
+{
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+        qop[g] = c16 < a.H ? *(const half8 *)(qrows + qrow_offset(c16, 4 * g + j)) : (half8)(_Float16)0.0f;
+}
+
+// Chunk k of token t: read the ids, publish them, and issue every gather of the
+// chunk (K rows into the wave's LDS tile, V rows and scales into registers).
+// Returns the ballot of valid slots; nothing is issued for an empty chunk.
+__device__ inline uint64_t issue_chunk(const AttnArgs &a, const WaveLds &L, int t, int k, int lane, int j, int c16,
+                                       uint2 &ks, uint2 &vs, uint2 (&vraw)[2][8])
+{
+    const int p = a.pos0 + t;
+    const int64_t slot = (int64_t)k * kChunk + lane;
+    int32_t id;
+    if (a.ids)
+        id = a.ids[(int64_t)t * a.ids_stride + slot];
+    else
+        id = slot <= p ? (int32_t)slot : -1;
     const bool valid = (uint32_t)id < (uint32_t)a.n_cells;
     const int32_t sid = valid ? id : 0;
     const uint64_t mask = __ballot(valid);
-    const bool work = mask != 0;                 // uniform over the wave
 
-    // ---- issue every gather of the chunk at once -----------------------------
-    s_id[lane] = sid;
+    L.id[lane] = sid;
     wave_sync_lds();
-    uint2 ks = make_uint2(0u, 0u), vs = make_uint2(0u, 0u);
-    uint2 vraw[2][8];
-    if (work) {
+    ks = make_uint2(0u, 0u);
+    vs = make_uint2(0u, 0u);
+    if (mask != 0) {
         if (valid) {
             ks = *(const uint2 *)(a.ksc + (int64_t)sid * 4);
             vs = *(const uint2 *)(a.vsc + (int64_t)sid * 4);
@@ -200,8 +204,8 @@ __global__ __launch_bounds__(64 * kWaves) void attn_kernel(AttnArgs a)
         for (int s = 0; s < 8; ++s) {
             const int row = 8 * s + (lane >> 3);
             const int lg = (lane & 7) ^ ((row >> 1) & 7);
-            const int8_t *src = a.kq + ((uint32_t)s_id[row] * kD + 16 * lg);   // n_cells * 128 < 2^32
-            __builtin_amdgcn_global_load_lds((const void *)src, (lds_void *)(ktile + 1024 * s), 16, 0, 0);
+            const int8_t *src = a.kq + ((uint32_t)L.id[row] * kD + 16 * lg);   // n_cells * 128 < 2^32
+            __builtin_amdgcn_global_load_lds((const void *)src, (lds_void *)(L.ktile + 1024 * s), 16, 0, 0);
         }
         // V: slot s of k-step ks is cell 32ks + 16(s/4) + 4j + s%4 -- the cells
         // whose scores this lane holds -- and the lane reads dims 8*c16 .. +7
@@ -210,26 +214,17 @@ __global__ __launch_bounds__(64 * kWaves) void attn_kernel(AttnArgs a)
 #pragma unroll
             for (int s = 0; s < 8; ++s) {
                 const int cell = 32 * ks2 + 16 * (s >> 2) + 4 * j + (s & 3);
-                vraw[ks2][s] = *(const uint2 *)(a.vq + ((uint32_t)s_id[cell] * kD + 8 * c16));
+                vraw[ks2][s] = *(const uint2 *)(a.vq + ((uint32_t)L.id[cell] * kD + 8 * c16));
             }
     }
-    // direct-to-LDS copies (q, K) complete, then the whole workgroup sees them
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
+    return mask;
+}
 
-    if (!has_chunk)
-        return;
-    const int64_t rec = ((int64_t)t * a.C + k) * a.H;
-    if (!work) {                     // empty chunk: (-inf, +0), o left alone
-        if (lane < a.H) {
-            a.m[rec + lane] = -INFINITY;
-            a.l[rec + lane] = 0.0f;
-        }
-        return;
-    }
-
-    // ---- scales: V scales may need a common power-of-two factor so that
-    // vq * vsc stays inside fp16 range ----------------------------------------
+// Publish the chunk's scales to LDS. V scales get a common power-of-two factor
+// when vq * vsc could leave fp16 range; returns that factor's inverse (1 when
+// no factor was needed) through `down` and whether one was applied.
+__device__ inline bool stage_scales(const WaveLds &L, int lane, uint2 ks, uint2 vs, float &down)
+{
     uint32_t ev = max(max((vs.x >> 10) & 31u, (vs.x >> 26) & 31u),
                       max((vs.y >> 10) & 31u, (vs.y >> 26) & 31u));
     uint32_t e = 0;                 // largest biased exponent in the chunk, bit by bit
@@ -241,9 +236,10 @@ __global__ __launch_bounds__(64 * kWaves) void attn_kernel(AttnArgs a)
     }
     // |vq| <= 127 and vsc < 2^(e - 14): no overflow below vsc = 2^9
     const bool renorm = e >= 24;
-    const float down = __int_as_float((127 - 15 + (int)e) << 23);   // 2^(e - 15)
+    down = 1.0f;
     uint2 vn = vs;
     if (renorm) {
+        down = __int_as_float((127 - 15 + (int)e) << 23);           // 2^(e - 15)
         const float up = __int_as_float((127 + 15 - (int)e) << 23); // 2^(15 - e)
         _Float16 h0 = (_Float16)(half_bits_to_float(vs.x & 0xffffu) * up);
         _Float16 h1 = (_Float16)(half_bits_to_float(vs.x >> 16) * up);
@@ -252,21 +248,20 @@ __global__ __launch_bounds__(64 * kWaves) void attn_kernel(AttnArgs a)
         vn.x = (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
         vn.y = (uint32_t)__builtin_bit_cast(uint16_t, h2) | ((uint32_t)__builtin_bit_cast(uint16_t, h3) << 16);
     }
-    s_ksc[lane] = ks;
-    s_vsc[0 * kChunk + lane] = (uint16_t)(vn.x & 0xffffu);
-    s_vsc[1 * kChunk + lane] = (uint16_t)(vn.x >> 16);
-    s_vsc[2 * kChunk + lane] = (uint16_t)(vn.y & 0xffffu);
-    s_vsc[3 * kChunk + lane] = (uint16_t)(vn.y >> 16);
+    L.ksc[lane] = ks;
+    L.vsc[0 * kChunk + lane] = (uint16_t)(vn.x & 0xffffu);
+    L.vsc[1 * kChunk + lane] = (uint16_t)(vn.x >> 16);
+    L.vsc[2 * kChunk + lane] = (uint16_t)(vn.y & 0xffffu);
+    L.vsc[3 * kChunk + lane] = (uint16_t)(vn.y >> 16);
     wave_sync_lds();
+    return renorm;
+}
 
-    // q operand: head c16, dims 32g + 8j .. +7 (zero for padding heads)
-    half8 qop[4];
-#pragma unroll
-    for (int g = 0; g < 4; ++g)
-        qop[g] = c16 < a.H ? *(const half8 *)(qrows + qrow_offset(c16, 4 * g + j)) : (half8)(_Float16)0.0f;
-
-    // ---- scores: S[b][r] is cell 16b + 4j + r, head c16 ----------------------
-    float S[4][4];
+// Scaled scores of the chunk: S[b][r] is cell 16b + 4j + r, head c16; empty
+// slots get -inf.
+__device__ inline void chunk_scores(float scale, const WaveLds &L, const half8 (&qop)[4], uint64_t mask, int j,
+                                    int c16, float (&S)[4][4])
+{
     const floatx4 zero = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
@@ -275,22 +270,25 @@ __global__ __launch_bounds__(64 * kWaves) void attn_kernel(AttnArgs a)
         const int row = 16 * b + c16;
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-            const uint2 kr = *(const uint2 *)(ktile + ktile_offset(row, 2 * g + (j >> 1)) + 8 * (j & 1));
+            const uint2 kr = *(const uint2 *)(L.ktile + ktile_offset(row, 2 * g + (j >> 1)) + 8 * (j & 1));
             acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(i8x8_to_half8(kr), qop[g], zero, 0, 0, 0);
         }
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int cell = 16 * b + 4 * j + r;
-            const uint2 kb = s_ksc[cell];
-            const float sv = a.scale * ((acc[0][r] * half_bits_to_float(kb.x & 0xffffu) +
-                                         acc[1][r] * half_bits_to_float(kb.x >> 16)) +
-                                        (acc[2][r] * half_bits_to_float(kb.y & 0xffffu) +
-                                         acc[3][r] * half_bits_to_float(kb.y >> 16)));
+            const uint2 kb = L.ksc[cell];
+            const float sv = scale * ((acc[0][r] * half_bits_to_float(kb.x & 0xffffu) +
+                                       acc[1][r] * half_bits_to_float(kb.x >> 16)) +
+                                      (acc[2][r] * half_bits_to_float(kb.y & 0xffffu) +
+                                       acc[3][r] * half_bits_to_float(kb.y >> 16)));
             S[b][r] = ((mask >> cell) & 1ull) ? sv : -INFINITY;
         }
     }
+}
 
-    // ---- chunk max and denominator per head ----------------------------------
+// Max over the chunk's cells for head c16 (the same value in all four rows j).
+__device__ inline float chunk_max(const float (&S)[4][4])
+{
     float mx = -INFINITY;
 #pragma unroll
     for (int b = 0; b < 4; ++b)
@@ -298,25 +296,28 @@ __global__ __launch_bounds__(64 * kWaves) void attn_kernel(AttnArgs a)
         for (int r = 0; r < 4; ++r)
             mx = fmaxf(mx, S[b][r]);
     mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    return fmaxf(mx, __shfl_xor(mx, 32, 64));
+}
 
-    float P[4][4];
+// p = exp(S - ref) for head c16, and their sum over the chunk.
+__device__ inline float chunk_probs(const float (&S)[4][4], float ref, float (&P)[4][4])
+{
     float lsum = 0.0f;
 #pragma unroll
     for (int b = 0; b < 4; ++b)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            P[b][r] = __builtin_amdgcn_exp2f((S[b][r] - mx) * kLog2e);   // exp(0) = 1 exactly
+            P[b][r] = __builtin_amdgcn_exp2f((S[b][r] - ref) * kLog2e);  // exp(0) = 1 exactly
             lsum += P[b][r];
         }
     lsum += __shfl_xor(lsum, 16, 64);
-    lsum += __shfl_xor(lsum, 32, 64);
+    return lsum + __shfl_xor(lsum, 32, 64);
+}
 
-    // ---- PV: O[tt] is heads 4j + r, dim 8*c16 + tt ---------------------------
-    floatx4 O[8];
-#pragma unroll
-    for (int tt = 0; tt < 8; ++tt)
-        O[tt] = zero;
+// O[tt] += p V over the chunk: O[tt] is heads 4j + r, dim 8*c16 + tt.
+__device__ inline void pv_accumulate(const float (&P)[4][4], const uint2 (&vraw)[2][8], const WaveLds &L, int j,
+                                     int c16, floatx4 (&O)[8])
+{
 #pragma unroll
     for (int ks2 = 0; ks2 < 2; ++ks2) {
         // A operand: p of slots s = cells 32ks + 16(s/4) + 4j + s%4, as hi + lo
@@ -333,7 +334,7 @@ __global__ __launch_bounds__(64 * kWaves) void attn_kernel(AttnArgs a)
 #pragma unroll
         for (int sp = 0; sp < 4; ++sp) {
             const int cell = 32 * ks2 + 16 * (sp >> 1) + 4 * j + 2 * (sp & 1);
-            sc[sp] = __builtin_bit_cast(half2v, *(const uint32_t *)&s_vsc[(c16 >> 2) * kChunk + cell]);
+            sc[sp] = __builtin_bit_cast(half2v, *(const uint32_t *)&L.vsc[(c16 >> 2) * kChunk + cell]);
         }
 #pragma unroll
         for (int tt = 0; tt < 8; ++tt) {
@@ -355,6 +356,66 @@ __global__ __launch_bounds__(64 * kWaves) void attn_kernel(AttnArgs a)
             O[tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa_lo, vb_hi, O[tt], 0, 0, 0);
         }
     }
+}
+
+// ---- chunk records (qsa_attn) ---------------------------------------------
+
+__global__ __launch_bounds__(64 * kWaves) void attn_kernel(AttnArgs a)
+{
+    extern __shared__ __align__(16) uint8_t lds[];
+
+    const int lane = threadIdx.x & 63;
+    const int w = threadIdx.x >> 6;
+    const int j = lane >> 4;        // 16-lane row of the wave
+    const int c16 = lane & 15;      // column inside a 16-wide MFMA tile
+
+    // each XCD (workgroup id mod 8) walks a contiguous range of workgroups
+    const int lb = (blockIdx.x & 7) * a.blocks_per_xcd + (blockIdx.x >> 3);
+    if (lb >= a.n_blocks)
+        return;                     // uniform over the workgroup
+    const int kg = lb / a.T;
+    const int t = lb - kg * a.T;
+    const int k = kWaves * kg + w;
+    const bool has_chunk = k < a.C;
+
+    const WaveLds L = wave_lds(lds, w);
+    uint8_t *qrows = lds + kWaves * kWaveBytes;
+
+    copy_q_rows(a, qrows, t, w, kWaves, lane);
+    uint2 ks = make_uint2(0u, 0u), vs = make_uint2(0u, 0u);
+    uint2 vraw[2][8];
+    uint64_t mask = 0;
+    if (has_chunk)
+        mask = issue_chunk(a, L, t, k, lane, j, c16, ks, vs, vraw);
+    // direct-to-LDS copies (q, K) complete, then the whole workgroup sees them
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+
+    if (!has_chunk)
+        return;
+    const int64_t rec = ((int64_t)t * a.C + k) * a.H;
+    if (mask == 0) {                 // empty chunk: (-inf, +0), o left alone
+        if (lane < a.H) {
+            a.m[rec + lane] = -INFINITY;
+            a.l[rec + lane] = 0.0f;
+        }
+        return;
+    }
+
+    float down;
+    const bool renorm = stage_scales(L, lane, ks, vs, down);
+    half8 qop[4];
+    q_operand(a, qrows, j, c16, qop);
+    float S[4][4];
+    chunk_scores(a.scale, L, qop, mask, j, c16, S);
+    const float mx = chunk_max(S);
+    float P[4][4];
+    const float lsum = chunk_probs(S, mx, P);
+    floatx4 O[8];
+#pragma unroll
+    for (int tt = 0; tt < 8; ++tt)
+        O[tt] = (floatx4){0.f, 0.f, 0.f, 0.f};
+    pv_accumulate(P, vraw, L, j, c16, O);
 
     // ---- write the chunk record ----------------------------------------------
     if (renorm) {                   // take the V scales' power of two back out, exactly
@@ -377,12 +438,140 @@ __global__ __launch_bounds__(64 * kWaves) void attn_kernel(AttnArgs a)
     }
 }
 
+// ---- attention with the merge in the same dispatch (qsa_attn_merge) --------
+//
+// One workgroup per token, nw = min(C, 4) waves; wave w takes chunks w, w + nw,
+// ... so every workgroup sweeps the chunks in the same order. A wave keeps a
+// running max M, denominator L and output O per head: a chunk with max m moves
+// M to max(M, m), its probabilities are taken against the new M and the old
+// (L, O) are rescaled by exp(M_old - M_new) -- the combination of chunk records
+// relative to the largest maximum, accumulated as it goes. The waves' (M, L, O)
+// are then combined the same way through LDS and divided once.
+
+__global__ __launch_bounds__(64 * kWaves) void attn_merge_kernel(AttnArgs a)
+{
+    extern __shared__ __align__(16) uint8_t lds[];
+
+    const int lane = threadIdx.x & 63;
+    const int w = threadIdx.x >> 6;
+    const int nw = blockDim.x >> 6;
+    const int j = lane >> 4;
+    const int c16 = lane & 15;
+
+    const int t = (blockIdx.x & 7) * a.blocks_per_xcd + (blockIdx.x >> 3);
+    if (t >= a.T)
+        return;                     // uniform over the workgroup
+
+    const WaveLds L = wave_lds(lds, w);
+    uint8_t *qrows = lds + nw * kWaveBytes;
+    copy_q_rows(a, qrows, t, w, nw, lane);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    half8 qop[4];
+    q_operand(a, qrows, j, c16, qop);
+
+    float Mrun = -INFINITY, Lrun = 0.0f;         // head c16
+    floatx4 O[8];                                // heads 4j + r, dim 8*c16 + tt
+#pragma unroll
+    for (int tt = 0; tt < 8; ++tt)
+        O[tt] = (floatx4){0.f, 0.f, 0.f, 0.f};
+
+    for (int k = w; k < a.C; k += nw) {
+        uint2 ks, vs;
+        uint2 vraw[2][8];
+        const uint64_t mask = issue_chunk(a, L, t, k, lane, j, c16, ks, vs, vraw);
+        __builtin_amdgcn_s_waitcnt(0);           // the K tile copy has landed
+        wave_sync_lds();
+        if (mask == 0)
+            continue;                            // uniform: an empty chunk adds nothing
+        float down;
+        const bool renorm = stage_scales(L, lane, ks, vs, down);
+        float S[4][4];
+        chunk_scores(a.scale, L, qop, mask, j, c16, S);
+        const float Mnew = fmaxf(Mrun, chunk_max(S));
+        const float alpha = __builtin_amdgcn_exp2f((Mrun - Mnew) * kLog2e);   // 0 for the first chunk
+        float P[4][4];
+        Lrun = fmaf(alpha, Lrun, chunk_probs(S, Mnew, P));
+        Mrun = Mnew;
+        // rescale O by alpha of its own heads (held by lanes c16 = 4j + r)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const float ar = __shfl(alpha, 4 * j + r, 64);
+#pragma unroll
+            for (int tt = 0; tt < 8; ++tt)
+                O[tt][r] *= ar;
+        }
+        if (renorm) {               // the chunk's V scales carry 2^(15 - e): put it back on p
+#pragma unroll
+            for (int b = 0; b < 4; ++b)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    P[b][r] *= down;
+        }
+        pv_accumulate(P, vraw, L, j, c16, O);
+        wave_sync_lds();                         // the tile is rewritten by the next chunk
+    }
+
+    // ---- combine the waves: (M, L) and O through LDS, then divide once ---
+    float *sM = (float *)L.ksc;                  // 16 floats
+    float *sL = sM + 16;                         // 16 floats
+    float *sO = (float *)L.ktile;                // [16 heads][128 dims]
+    if (j == 0) {
+        sM[c16] = Mrun;
+        sL[c16] = Lrun;
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        float *dst = sO + (4 * j + r) * kD + 8 * c16;
+        *(float4 *)dst = make_float4(O[0][r], O[1][r], O[2][r], O[3][r]);
+        *(float4 *)(dst + 4) = make_float4(O[4][r], O[5][r], O[6][r], O[7][r]);
+    }
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < a.H * (kD / 4); idx += blockDim.x) {
+        const int h = idx / (kD / 4), d4 = idx - h * (kD / 4);
+        float M = -INFINITY;
+        for (int v = 0; v < nw; ++v)
+            M = fmaxf(M, ((const float *)wave_lds(lds, v).ksc)[h]);
+        uint2 res = make_uint2(0u, 0u);          // +0 when no slot of the row was valid
+        if (M != -INFINITY) {
+            float Ls = 0.0f;
+            float4 Os = make_float4(0.f, 0.f, 0.f, 0.f);
+            for (int v = 0; v < nw; ++v) {
+                const WaveLds Lv = wave_lds(lds, v);
+                const float mv = ((const float *)Lv.ksc)[h];
+                if (mv == -INFINITY)
+                    continue;
+                const float wv = __builtin_amdgcn_exp2f((mv - M) * kLog2e);
+                Ls = fmaf(wv, ((const float *)Lv.ksc)[16 + h], Ls);
+                const float4 ov = *(const float4 *)((const float *)Lv.ktile + h * kD + 4 * d4);
+                Os.x = fmaf(wv, ov.x, Os.x);
+                Os.y = fmaf(wv, ov.y, Os.y);
+                Os.z = fmaf(wv, ov.z, Os.z);
+                Os.w = fmaf(wv, ov.w, Os.w);
+            }
+            const _Float16 r0 = (_Float16)(Os.x / Ls), r1 = (_Float16)(Os.y / Ls);
+            const _Float16 r2 = (_Float16)(Os.z / Ls), r3 = (_Float16)(Os.w / Ls);
+            res.x = (uint32_t)__builtin_bit_cast(uint16_t, r0) | ((uint32_t)__builtin_bit_cast(uint16_t, r1) << 16);
+            res.y = (uint32_t)__builtin_bit_cast(uint16_t, r2) | ((uint32_t)__builtin_bit_cast(uint16_t, r3) << 16);
+        }
+        *(uint2 *)(a.out + ((int64_t)t * a.H + h) * kD + 4 * d4) = res;
+    }
+}
+
 } // namespace
 
 hipError_t launch_attn(const AttnArgs &a, hipStream_t stream)
 {
     dim3 grid(8 * a.blocks_per_xcd), block(64 * kWaves);
-    hipLaunchKernelGGL(attn_kernel, grid, block, attn_lds_bytes(a.H), stream, a);
+    hipLaunchKernelGGL(attn_kernel, grid, block, attn_lds_bytes(kWaves, a.H), stream, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_attn_merge(const AttnArgs &a, hipStream_t stream)
+{
+    const int nw = a.C < kWaves ? a.C : kWaves;
+    dim3 grid(8 * a.blocks_per_xcd), block(64 * nw);
+    hipLaunchKernelGGL(attn_merge_kernel, grid, block, attn_lds_bytes(nw, a.H), stream, a);
     return hipGetLastError();
 }
 

@@ -24,9 +24,10 @@ struct AttnArgs {
     int64_t ids_stride;
     int32_t n_cells, pos0, T, H, C;
     float scale;
-    float *o;                 // [T][C][H][D]
+    float *o;                 // [T][C][H][D]   chunk records (qsa_attn)
     float *m;                 // [T][C][H]
     float *l;                 // [T][C][H]
+    _Float16 *out;            // [T][H][D]      merged output (qsa_attn_merge)
     int32_t n_blocks;         // workgroups that carry work: ceil(C / 4) chunk groups x T tokens
     int32_t blocks_per_xcd;   // workgroups each XCD walks through
 };
@@ -60,6 +61,7 @@ inline void part_layout(int64_t T, int64_t H, int64_t D, int64_t C,
 }
 
 hipError_t launch_attn(const AttnArgs &a, hipStream_t stream);
+hipError_t launch_attn_merge(const AttnArgs &a, hipStream_t stream);
 hipError_t launch_merge(const MergeArgs &a, hipStream_t stream);
 hipError_t launch_score(const ScoreArgs &a, hipStream_t stream);
 

@@ -196,3 +196,29 @@ def check_score_case(sc: synth.ScoreCase, n_sample=16, seed=0):
         assert np.all(err <= lim), "score row %d: max err/lim %g" % (t, (err / lim).max())
         worst = max(worst, float((err / np.maximum(A, 1e-30)).max()))
     return worst
+
+
+def run_fused(layer: synth.Layer, ids, pos0, scale, implicit=False):
+    """Run qsa_attn_merge on the GPU; returns the fp16 output as numpy."""
+    T, H, D = layer.q.shape
+    q, kq, vq = to_dev(layer.q), to_dev(layer.kq), to_dev(layer.vq)
+    ksc, vsc = to_dev(layer.ksc), to_dev(layer.vsc)
+    ids_t = None if implicit else to_dev(ids)
+    out = torch.full((T, H, D), float("nan"), dtype=torch.float16, device=dev())
+    qsa.qsa_attn_merge(q, kq, vq, ksc, vsc, ids_t, pos0, float(scale), out)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+def check_fused_case(case: synth.AttnCase, n_sample=20, implicit=False, seed=0):
+    """qsa_attn_merge vs the oracle on sampled tokens of every layer of a case."""
+    toks = sample_tokens(case.T, n_sample, seed)
+    worst = (0.0, 0.0)
+    for li, L in enumerate(case.layers):
+        out = run_fused(L, case.ids, case.pos0, case.scale, implicit=implicit)
+        assert not np.any(np.isnan(out)), "NaN output %s layer %d" % (case.name, li)
+        refs = oracle_tokens(L, None if implicit else case.ids, case.pos0, case.scale, toks)
+        for t in toks:
+            e = check_out(out[t], refs[t]["out64"], "fused %s layer %d t=%d" % (case.name, li, t))
+            worst = (max(worst[0], e[0]), max(worst[1], e[1]))
+    return worst

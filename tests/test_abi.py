@@ -24,7 +24,7 @@ def declared_symbols():
 def test_library_loads_and_exports_every_declared_symbol():
     L = qsa.lib()
     names = declared_symbols()
-    assert {"qsa_attn", "qsa_merge", "qsa_score", "qsa_part_bytes", "qsa_part_offsets",
+    assert {"qsa_attn", "qsa_attn_merge", "qsa_merge", "qsa_score", "qsa_part_bytes", "qsa_part_offsets",
             "qsa_last_error"} <= names
     for n in names:
         assert hasattr(L, n), n
@@ -160,3 +160,34 @@ def test_binding_refuses_host_tensors():
     sc = torch.ones(4, 4, dtype=torch.float16)
     with pytest.raises(ValueError):
         qsa.qsa_attn(q, kq, kq, sc, sc, None, 2, 0.1, torch.zeros(1 << 16, dtype=torch.uint8))
+
+
+def attn_merge(**kw):
+    a = dict(q=FAKE, kq=FAKE, vq=FAKE, ksc=FAKE, vsc=FAKE, n_cells=100, ids=FAKE, ids_stride=64,
+             pos0=10, T=4, H=12, D=128, scale=0.1, out=FAKE)
+    a.update(kw)
+    P = ctypes.c_void_p
+    return qsa.lib().qsa_attn_merge(P(a["q"]), P(a["kq"]), P(a["vq"]), P(a["ksc"]), P(a["vsc"]), a["n_cells"],
+                                    P(a["ids"]), a["ids_stride"], a["pos0"], a["T"], a["H"], a["D"], a["scale"],
+                                    P(a["out"]), P(None))
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(T=-1), qsa.QSA_ERR_ARG),
+    (dict(H=0), qsa.QSA_ERR_ARG),
+    (dict(H=17), qsa.QSA_ERR_UNSUPPORTED),
+    (dict(D=64), qsa.QSA_ERR_UNSUPPORTED),
+    (dict(ids_stride=32), qsa.QSA_ERR_ARG),
+    (dict(n_cells=(1 << 25) + 1), qsa.QSA_ERR_UNSUPPORTED),
+    (dict(out=None), qsa.QSA_ERR_ARG),
+    (dict(out=FAKE + 8), qsa.QSA_ERR_ARG),
+    (dict(q=None), qsa.QSA_ERR_ARG),
+    (dict(ksc=FAKE + 4), qsa.QSA_ERR_ARG),
+])
+def test_attn_merge_rejects_bad_arguments_on_host(kw, status):
+    assert attn_merge(**kw) == status
+    assert qsa.qsa_last_error().startswith("qsa_attn_merge")
+
+
+def test_attn_merge_zero_tokens_is_a_no_op():
+    assert attn_merge(T=0, q=None, out=None) == qsa.QSA_OK

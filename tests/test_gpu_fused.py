@@ -1,0 +1,133 @@
+"""GPU parity of qsa_attn_merge (attention and merge in one dispatch) against
+the CPU oracle, through the C ABI."""
+import numpy as np
+import pytest
+
+from sparse_selection_attention_amd import synth
+
+from gpu_util import (check_fused_case, check_out, oracle_token, oracle_tokens, run_attn, run_fused)
+from test_gpu_attn import probe_case
+
+pytestmark = pytest.mark.gpu
+
+
+def test_fused_tiny_all_tokens():
+    case = synth.tiny()
+    out = run_fused(case.layers[0], case.ids, case.pos0, case.scale)
+    for t in range(case.T):
+        r = oracle_token(case.layers[0], case.ids, case.pos0, case.scale, t)
+        check_out(out[t], r["out64"], "fused tiny t=%d" % t)
+
+
+@pytest.mark.parametrize("ntok", [1, 2, 5, 8])
+def test_fused_mtp_decode_window(ntok):
+    print("fused mtp", ntok, check_fused_case(synth.mtp(ntok)), flush=True)
+
+
+def test_fused_prompt_start_explicit_and_implicit():
+    case = synth.prompt_start()
+    print("fused prompt", check_fused_case(case, n_sample=12), flush=True)
+    print("fused prompt implicit", check_fused_case(case, n_sample=12, implicit=True), flush=True)
+
+
+def test_fused_mid_context_three_layers():
+    print("fused mid", check_fused_case(synth.mid(layers=3), n_sample=10), flush=True)
+
+
+def test_fused_long_context_three_layers():
+    print("fused long", check_fused_case(synth.long_ctx(layers=3), n_sample=10), flush=True)
+
+
+@pytest.mark.parametrize("variant", ["signed_zero", "cancel"])
+def test_fused_long_context_edge_variants(variant):
+    case = synth.long_ctx(layers=1, variant=variant)
+    L = case.layers[0]
+    out = run_fused(L, case.ids, case.pos0, case.scale)
+    toks = [0, 4] if variant == "signed_zero" else [1, 5]
+    heads = [0, 6] if variant == "signed_zero" else list(range(12))
+    for t in toks:
+        row = case.ids[t]
+        cells = row[row >= 0]
+        mean = (L.vq[cells].astype(np.float64) * np.repeat(L.vsc[cells].astype(np.float64), 32, axis=1)).mean(0)
+        for h in heads:
+            check_out(out[t, h], mean, "fused %s t=%d h=%d" % (variant, t, h))
+
+
+def test_fused_matches_two_kernel_path():
+    """Both paths approximate the same values; they agree far inside the output tolerance."""
+    case = synth.long_ctx(layers=1, T=256)
+    L = case.layers[0]
+    a = run_attn(L, case.ids, case.pos0, case.scale)[0].astype(np.float64)
+    b = run_fused(L, case.ids, case.pos0, case.scale).astype(np.float64)
+    assert np.abs(a - b).max() <= 2e-4
+
+
+def test_fused_probe_case_all_tokens():
+    L, ids, pos0 = probe_case(seed=11)
+    out = run_fused(L, ids, pos0, synth.SCALE_1_SQRT_128)
+    refs = oracle_tokens(L, ids, pos0, synth.SCALE_1_SQRT_128, list(range(ids.shape[0])))
+    for t, r in refs.items():
+        check_out(out[t], r["out64"], "fused probe t=%d" % t)
+    assert np.all(out[7].view(np.uint16) == 0)    # the row with no valid slot is +0
+
+
+def test_fused_one_cell_selection_is_bitwise():
+    T, H, n_cells = 64, 12, 300
+    L = synth.make_layer(4, 0, T, H, n_cells)
+    rng = np.random.default_rng(1)
+    ids = np.full((T, 320), -1, dtype=np.int32)
+    cells = rng.integers(0, n_cells - T, T)
+    ids[np.arange(T), rng.integers(0, 320, T)] = cells
+    out = run_fused(L, ids, n_cells - T, synth.SCALE_1_SQRT_128)
+    v = L.vq[cells].astype(np.float64) * np.repeat(L.vsc[cells].astype(np.float64), 32, axis=1)
+    assert np.array_equal(out.view(np.uint16), np.repeat(v.astype(np.float16)[:, None, :], H, axis=1).view(np.uint16))
+
+
+def test_fused_poison_and_unselected_data_do_not_matter():
+    L, ids, pos0 = probe_case(seed=12)
+    n_cells = L.kq.shape[0]
+    a = run_fused(L, ids, pos0, synth.SCALE_1_SQRT_128)
+    used = np.zeros(n_cells, bool)
+    used[ids[(ids >= 0) & (ids < n_cells)]] = True
+    L2 = synth.Layer(L.q.copy(), L.kq.copy(), L.vq.copy(), L.ksc.copy(), L.vsc.copy())
+    L2.kq[~used] = -127
+    L2.vq[~used] = 127
+    L2.ksc[~used] = 30000.0
+    L2.vsc[~used] = 500.0
+    ids2 = ids.copy()
+    ids2[(ids2 < 0) | (ids2 >= n_cells)] = -1
+    b = run_fused(L2, ids2, pos0, synth.SCALE_1_SQRT_128)
+    assert np.array_equal(a.view(np.uint16), b.view(np.uint16))
+
+
+def test_fused_determinism():
+    L, ids, pos0 = probe_case(seed=13)
+    a = run_fused(L, ids, pos0, synth.SCALE_1_SQRT_128)
+    b = run_fused(L, ids, pos0, synth.SCALE_1_SQRT_128)
+    assert np.array_equal(a.view(np.uint16), b.view(np.uint16))
+
+
+@pytest.mark.parametrize("T,H,n_cells,pos0", [(1, 1, 1, 0), (1, 16, 65, 64), (5, 7, 130, 125), (70, 16, 200, 130),
+                                             (33, 2, 64, 31), (3, 12, 250, 247)])
+def test_fused_edge_shapes_implicit_rows(T, H, n_cells, pos0):
+    L = synth.make_layer(T + H + 1, 0, T, H, n_cells)
+    out = run_fused(L, None, pos0, synth.SCALE_1_SQRT_128, implicit=True)
+    for t in range(T):
+        r = oracle_token(L, None, pos0, synth.SCALE_1_SQRT_128, t)
+        check_out(out[t], r["out64"], "fused edge t=%d" % t)
+
+
+def test_fused_large_and_tiny_scales():
+    L, ids, pos0 = probe_case(T=40, seed=14)
+    base = L.vsc.astype(np.float32)
+    L.vsc[:] = (base * 10000).astype(np.float16)
+    L.vsc[::3] = (base[::3] * 1e-3).astype(np.float16)
+    L.ksc[:5] = np.float16(2.0 ** -24)
+    L.q[:] = (L.q.astype(np.float32) * 40).astype(np.float16)
+    out = run_fused(L, ids, pos0, np.float32(1.0))
+    refs = oracle_tokens(L, ids, pos0, np.float32(1.0), list(range(40)))
+    for t, r in refs.items():
+        scale_out = max(1.0, float(np.abs(r["out64"]).max()))
+        g = out[t].astype(np.float64)
+        assert np.all(np.isfinite(g))
+        assert np.abs(g - r["out64"]).max() <= 2e-3 * scale_out
