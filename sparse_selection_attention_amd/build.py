@@ -7,6 +7,7 @@ from __future__ import annotations
 
 import glob
 import os
+import re
 import subprocess
 import sys
 
@@ -36,12 +37,44 @@ def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
 
 
+def kernel_resources(remarks: str) -> dict:
+    """Per-kernel VGPRs, scratch bytes per lane and occupancy, parsed from the
+    compiler's kernel-resource-usage remarks."""
+    out, name = {}, None
+    for line in remarks.splitlines():
+        m = re.search(r"remark: Function Name: (\S+)", line)
+        if m:
+            name = m.group(1)
+            out[name] = {}
+            continue
+        m = re.search(r"remark:\s+(VGPRs|ScratchSize \[bytes/lane\]|Occupancy \[waves/SIMD\]): (\d+)", line)
+        if m and name:
+            out[name][m.group(1).split()[0]] = int(m.group(2))
+    return out
+
+
 def build(verbose: bool = False) -> str:
-    cmd = [HIPCC] + FLAGS + ["-I", os.path.join(ROOT, "include"), "-I", CSRC] + sources() + [
-        "-o", LIB + ".tmp"]
+    cmd = [HIPCC] + FLAGS + ["-Rpass-analysis=kernel-resource-usage",
+                             "-I", os.path.join(ROOT, "include"), "-I", CSRC] + sources() + ["-o", LIB + ".tmp"]
     if verbose:
         print(" ".join(cmd), flush=True)
-    subprocess.run(cmd, check=True)
+    r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True)
+    remarks = r.stdout + r.stderr
+    if r.returncode != 0:
+        sys.stderr.write("\n".join(l for l in remarks.splitlines() if "remark:" not in l) + "\n")
+        raise subprocess.CalledProcessError(r.returncode, cmd)
+    res = kernel_resources(remarks)
+    if not res:
+        raise RuntimeError("no kernel-resource-usage remarks from %s" % HIPCC)
+    # every kernel keeps its state in registers and LDS: a register spill to
+    # scratch is a build error, not a silent slowdown
+    spills = {k: v for k, v in res.items() if v.get("ScratchSize", 0) != 0}
+    if spills:
+        os.remove(LIB + ".tmp")
+        raise RuntimeError("kernels spill to scratch: %s" % spills)
+    if verbose:
+        for k, v in sorted(res.items()):
+            print(k, v, flush=True)
     os.replace(LIB + ".tmp", LIB)
     return LIB
 

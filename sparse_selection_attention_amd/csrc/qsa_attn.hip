@@ -452,11 +452,9 @@ __global__ __launch_bounds__(64 * kWaves) void attn_merge_kernel(AttnArgs a)
 {
     extern __shared__ __align__(16) uint8_t lds[];
 
-    const int lane = threadIdx.x & 63;
+    const int lane0 = threadIdx.x & 63;
     const int w = threadIdx.x >> 6;
     const int nw = blockDim.x >> 6;
-    const int j = lane >> 4;
-    const int c16 = lane & 15;
 
     const int t = (blockIdx.x & 7) * a.blocks_per_xcd + (blockIdx.x >> 3);
     if (t >= a.T)
@@ -464,11 +462,9 @@ __global__ __launch_bounds__(64 * kWaves) void attn_merge_kernel(AttnArgs a)
 
     const WaveLds L = wave_lds(lds, w);
     uint8_t *qrows = lds + nw * kWaveBytes;
-    copy_q_rows(a, qrows, t, w, nw, lane);
+    copy_q_rows(a, qrows, t, w, nw, lane0);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    half8 qop[4];
-    q_operand(a, qrows, j, c16, qop);
 
     float Mrun = -INFINITY, Lrun = 0.0f;         // head c16
     floatx4 O[8];                                // heads 4j + r, dim 8*c16 + tt
@@ -477,6 +473,11 @@ __global__ __launch_bounds__(64 * kWaves) void attn_merge_kernel(AttnArgs a)
         O[tt] = (floatx4){0.f, 0.f, 0.f, 0.f};
 
     for (int k = w; k < a.C; k += nw) {
+        // lane-derived offsets are rebuilt every chunk (cheap VALU) rather than
+        // hoisted out of the loop, where they would pin registers throughout
+        int lane = lane0;
+        asm volatile("" : "+v"(lane));
+        const int j = lane >> 4, c16 = lane & 15;
         uint2 ks, vs;
         uint2 vraw[2][8];
         const uint64_t mask = issue_chunk(a, L, t, k, lane, j, c16, ks, vs, vraw);
@@ -486,6 +487,8 @@ __global__ __launch_bounds__(64 * kWaves) void attn_merge_kernel(AttnArgs a)
             continue;                            // uniform: an empty chunk adds nothing
         float down;
         const bool renorm = stage_scales(L, lane, ks, vs, down);
+        half8 qop[4];
+        q_operand(a, qrows, j, c16, qop);
         float S[4][4];
         chunk_scores(a.scale, L, qop, mask, j, c16, S);
         const float Mnew = fmaxf(Mrun, chunk_max(S));
@@ -513,6 +516,7 @@ __global__ __launch_bounds__(64 * kWaves) void attn_merge_kernel(AttnArgs a)
     }
 
     // ---- combine the waves: (M, L) and O through LDS, then divide once ---
+    const int j = lane0 >> 4, c16 = lane0 & 15;
     float *sM = (float *)L.ksc;                  // 16 floats
     float *sL = sM + 16;                         // 16 floats
     float *sO = (float *)L.ktile;                // [16 heads][128 dims]

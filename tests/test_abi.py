@@ -191,3 +191,19 @@ def test_attn_merge_rejects_bad_arguments_on_host(kw, status):
 
 def test_attn_merge_zero_tokens_is_a_no_op():
     assert attn_merge(T=0, q=None, out=None) == qsa.QSA_OK
+
+
+def test_build_rejects_spilling_kernels():
+    from sparse_selection_attention_amd import build
+    text = "\n".join([
+        "a.hip:1:1: remark: Function Name: kern_a [-Rpass-analysis=kernel-resource-usage]",
+        "a.hip:1:1: remark:     VGPRs: 120 [-Rpass-analysis=kernel-resource-usage]",
+        "a.hip:1:1: remark:     ScratchSize [bytes/lane]: 0 [-Rpass-analysis=kernel-resource-usage]",
+        "a.hip:1:1: remark:     Occupancy [waves/SIMD]: 4 [-Rpass-analysis=kernel-resource-usage]",
+        "a.hip:9:1: remark: Function Name: kern_b [-Rpass-analysis=kernel-resource-usage]",
+        "a.hip:9:1: remark:     VGPRs: 128 [-Rpass-analysis=kernel-resource-usage]",
+        "a.hip:9:1: remark:     ScratchSize [bytes/lane]: 60 [-Rpass-analysis=kernel-resource-usage]",
+    ])
+    res = build.kernel_resources(text)
+    assert res == {"kern_a": {"VGPRs": 120, "ScratchSize": 0, "Occupancy": 4},
+                   "kern_b": {"VGPRs": 128, "ScratchSize": 60}}
