@@ -51,6 +51,8 @@ def lib():
         L.qso_score.argtypes = [P, P, i32, i32, i32, i32, i32, _ct.c_double, _ct.c_double,
                                 P, _ct.c_int64, i32, i32]
         L.qso_score.restype = _ct.c_int
+        L.qso_quant_rows.argtypes = [P, i32, i32, P, P]
+        L.qso_quant_rows.restype = _ct.c_int
         _lib = L
     return _lib
 
@@ -163,3 +165,15 @@ def _run_ranges(fn, ranges):
     with _cf.ThreadPoolExecutor(len(ranges)) as ex:
         for f in [ex.submit(fn, r) for r in ranges]:
             f.result()
+
+
+def quant_rows(x):
+    """Int8 codes and fp16 scale bits (uint16) of fp32 rows x[n][D], one scale
+    per 32-element group (qso_quant_rows)."""
+    x = _np.ascontiguousarray(x, dtype=_np.float32)
+    n, D = x.shape
+    codes = _np.zeros((n, D), dtype=_np.int8)
+    scales = _np.zeros((n, D // 32), dtype=_np.uint16)
+    if lib().qso_quant_rows(_ptr(x), n, D, _ptr(codes), _ptr(scales)) != 0:
+        raise ValueError("qso_quant_rows: bad arguments")
+    return codes, scales

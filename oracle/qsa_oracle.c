@@ -43,6 +43,20 @@
  *    scale * sum_h sum_d q[t][h][d] * k[c][d] for c <= p; the rest of the
  *    64-cell tile that holds cell p (and lies inside the row) gets `dead`;
  *    every later cell is left as it was.
+ *  qso_quant_rows -- the int8 cache rows the attention reads, with one fp16
+ *    scale per 32-element group ("round 11 track b: qsa attention and score",
+ *    section "implementation and evaluator": four scale groups per K row; the
+ *    prep step that writes kq/vq/ksc/vsc is memory bound on the rows it reads
+ *    and writes: "Round 36 Track C ...", section "Summary & Decision"). The
+ *    pages do not print the rule; the reading taken is symmetric absmax:
+ *      a = max |x_d| over the group,
+ *      s = fp16_RNE(fp32(a / 127)),
+ *      code_d = clamp(rint(fp32(x_d / s)), -127, 127), or 0 when s == 0.
+ *    Both quotients are binary32 quotients rounded to nearest even; rint
+ *    rounds half to even. The quotient is computed in binary64 and rounded to
+ *    binary32: with 53 >= 2 * 24 + 2 bits that double rounding gives the
+ *    correctly rounded binary32 quotient (Figueroa, "When is double rounding
+ *    innocuous?", 1995).
  */
 #include <math.h>
 #include <stddef.h>
@@ -255,6 +269,46 @@ int qso_score(const float *q, const float *k, int32_t n_cells, int32_t pos0, int
             tile_end = row_stride;
         for (int64_t c = p + 1; c < tile_end; ++c)
             row[c] = dead;
+    }
+    return 0;
+}
+
+/* ---- int8 cache rows with per-32 fp16 scales ---------------------------------- */
+
+static float quotient_f32(float num, float den)
+{
+    return (float)((double)num / (double)den);
+}
+
+int qso_quant_rows(const float *x, int32_t n_rows, int32_t D, int8_t *codes, uint16_t *scales)
+{
+    if (n_rows < 0 || D <= 0 || D % QSO_GROUP != 0)
+        return 1;
+    const int32_t G = D / QSO_GROUP;
+    for (int64_t r = 0; r < n_rows; ++r) {
+        for (int32_t g = 0; g < G; ++g) {
+            const float *xg = x + r * D + (int64_t)g * QSO_GROUP;
+            int8_t *cg = codes + r * D + (int64_t)g * QSO_GROUP;
+            float a = 0.0f;
+            for (int i = 0; i < QSO_GROUP; ++i)
+                if (fabsf(xg[i]) > a)
+                    a = fabsf(xg[i]);
+            const float s32 = quotient_f32(a, 127.0f);
+            const uint16_t s16 = qso_double_to_half((double)s32);
+            scales[r * G + g] = s16;
+            const float s = (float)qso_half_to_double(s16);
+            for (int i = 0; i < QSO_GROUP; ++i) {
+                float c = 0.0f;
+                if (s > 0.0f) {
+                    c = rintf(quotient_f32(xg[i], s));
+                    if (c > 127.0f)
+                        c = 127.0f;
+                    if (c < -127.0f)
+                        c = -127.0f;
+                }
+                cg[i] = (int8_t)c;
+            }
+        }
     }
     return 0;
 }
