@@ -9,8 +9,9 @@ one stream, with every input resident in HBM before the timed region.
 
 Prints one JSON line: query-token*heads per second, achieved algorithmic GB/s,
 the roofline of the dominant kernel (qsa_attn) measured with HIP events inside
-the timed region, the companion causal-score kernel, and the CPU oracle timed
-on a bounded sample on this host's cores.
+the timed region, the single-dispatch attention + merge, the companion
+causal-score kernel, the int8 cache writer, and the CPU oracle timed on a
+bounded sample on this host's cores.
 """
 from __future__ import annotations
 
@@ -106,6 +107,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
     ap.add_argument("--no-score", action="store_true", help="skip the companion score kernel")
     ap.add_argument("--no-fused", action="store_true", help="skip the single-dispatch attention + merge line")
+    ap.add_argument("--no-quant", action="store_true", help="skip the int8 cache writer line")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="also run one device copy of this many MiB (for counter calibration)")
     args = ap.parse_args()
@@ -264,6 +266,43 @@ def main():
                          "unit": "TFLOP/s", "frac": flops / (us * 1e-6) / 1e12 / FP32_MFMA_PEAK_TFLOPS},
         }
         del scores
+
+    if not args.no_quant:
+        # int8 cache writer: fp32 K and V rows -> int8 rows + per-32 fp16 scales.
+        # Algorithmic bytes per row pair: 2 x 512 read + 2 x (128 + 8) written.
+        def time_quant(rows, reps):
+            xk = up(synth.cache_rows(rows, which=0))
+            xv = up(synth.cache_rows(rows, which=1))
+            ckq = torch.empty(rows, D, dtype=torch.int8, device=dev)
+            cvq = torch.empty_like(ckq)
+            cks = torch.empty(rows, D // 32, dtype=torch.float16, device=dev)
+            cvs = torch.empty_like(cks)
+            for _ in range(2):
+                qsa.qsa_quant_append(xk, xv, ckq, cvq, cks, cvs, 0, stream=stream)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(reps):
+                qsa.qsa_quant_append(xk, xv, ckq, cvq, cks, cvs, 0, stream=stream)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1e3 / reps
+            return us, rows * 2 * (4 * D + D + 2 * (D // 32))
+
+        big_rows = 1 << 18
+        us_big, b_big = time_quant(big_rows, 20)
+        us_layer, b_layer = time_quant(case.n_cells, 50)
+        us_prompt, _ = time_quant(T, 50)
+        gbs = b_big / (us_big * 1e-6) / 1e9
+        result["cache_producer"] = {
+            "entry": "qsa_quant_append",
+            "workload": "262144 K and V rows (a 256k-cell cache, 340 MB moved, more than the Infinity Cache holds)",
+            "avg_us": us_big,
+            "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": gbs / HBM_PEAK_GBS},
+            "long_context_layer_31984_rows_us": us_layer,
+            "long_context_layer_gbs": b_layer / (us_layer * 1e-6) / 1e9,
+            "prompt_1984_rows_us": us_prompt,
+        }
 
     if args.copy_calibration:
         # one elementwise kernel that reads n bytes and writes n bytes

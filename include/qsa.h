@@ -153,6 +153,35 @@ QSA_API qsa_status qsa_score(const float *q, const float *k, int32_t n_cells, in
                      int32_t T, int32_t Hs, int32_t D, float scale, float dead,
                      float *scores, int64_t row_stride, void *stream);
 
+/*
+ * qsa_quant_append -- write fp32 K and V rows into the int8 cache with one
+ * fp16 scale per 32-element group.
+ *
+ * The cache format is the one the attention reads ("round 11 track b: qsa
+ * attention and score", section "implementation and evaluator": four scale
+ * groups per K row); the pages' prep step writes it ("Round 36 Track C ...",
+ * section "Summary & Decision") but does not print its rule. The rule taken,
+ * for each row i and each 32-element group:
+ *   a = max |x|,  s = fp16_rne(a / 127),
+ *   code = clamp(rint(x / s), -127, 127), or 0 when s == 0,
+ * with both quotients correctly rounded binary32 divisions and rint rounding
+ * half to even. Row i of k lands in kq[cell0 + i] and ksc[cell0 + i], row i of
+ * v in vq[cell0 + i] and vsc[cell0 + i]; no other cell is written. Inputs are
+ * expected finite: a group whose a / 127 exceeds the fp16 range gets an
+ * infinite scale and zero codes.
+ *
+ * k, v          fp32 [n_rows][D], 16-byte aligned (read only)
+ * kq, vq        int8 [n_cells_cap][D], 8-byte aligned
+ * ksc, vsc      fp16 [n_cells_cap][D/32], 8-byte aligned
+ * cell0         first cell written; cell0 + n_rows <= n_cells_cap
+ * D             this build implements D == 128 only
+ * n_rows == 0 is a no-op. Bad arguments return QSA_ERR_ARG / QSA_ERR_UNSUPPORTED
+ * before anything is enqueued.
+ */
+QSA_API qsa_status qsa_quant_append(const float *k, const float *v, int32_t n_rows, int32_t D,
+                            int8_t *kq, int8_t *vq, void *ksc, void *vsc,
+                            int32_t cell0, int32_t n_cells_cap, void *stream);
+
 /* Bytes of the `part` workspace for T tokens, H heads, head dim D, n_chunks chunks. */
 QSA_API size_t qsa_part_bytes(int32_t T, int32_t H, int32_t D, int32_t n_chunks);
 

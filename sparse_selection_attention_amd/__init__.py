@@ -16,7 +16,8 @@ import torch
 
 __all__ = [
     "QsaError", "CHUNK", "GROUP", "HEAD_DIM",
-    "qsa_attn", "qsa_attn_merge", "qsa_merge", "qsa_score", "qsa_part_bytes", "qsa_part_offsets", "qsa_last_error",
+    "qsa_attn", "qsa_attn_merge", "qsa_merge", "qsa_score", "qsa_quant_append", "qsa_part_bytes", "qsa_part_offsets",
+    "qsa_last_error",
     "alloc_part", "part_views", "chunk_count", "lib", "LIB_PATH",
 ]
 
@@ -54,6 +55,8 @@ def lib() -> ctypes.CDLL:
         L.qsa_merge.restype = ctypes.c_int
         L.qsa_score.argtypes = [P, P, i32, i32, i32, i32, i32, f32, f32, P, i64, P]
         L.qsa_score.restype = ctypes.c_int
+        L.qsa_quant_append.argtypes = [P, P, i32, i32, P, P, P, P, i32, i32, P]
+        L.qsa_quant_append.restype = ctypes.c_int
         L.qsa_part_bytes.argtypes = [i32, i32, i32, i32]
         L.qsa_part_bytes.restype = ctypes.c_size_t
         L.qsa_part_offsets.argtypes = [i32, i32, i32, i32, ctypes.POINTER(ctypes.c_size_t),
@@ -205,3 +208,25 @@ def qsa_score(q: torch.Tensor, k: torch.Tensor, pos0: int, scale: float, dead: f
         raise ValueError("scores must have T rows")
     _raise_on(lib().qsa_score(_ptr(q), _ptr(k), k.shape[0], pos0, T, Hs, D, float(scale), float(dead),
                               _ptr(scores), scores.shape[1], _stream(stream)))
+
+
+def qsa_quant_append(k: torch.Tensor, v: torch.Tensor, kq: torch.Tensor, vq: torch.Tensor, ksc: torch.Tensor,
+                     vsc: torch.Tensor, cell0: int, stream=None) -> None:
+    """Quantise fp32 rows k, v [n][D] into the int8 cache at cells cell0 .. cell0 + n - 1
+    (kq, vq int8 [cap][D]; ksc, vsc fp16 [cap][D/32]), one fp16 scale per 32 elements."""
+    _need(k, "k", torch.float32, 2)
+    _need(v, "v", torch.float32, 2)
+    _need(kq, "kq", torch.int8, 2)
+    _need(vq, "vq", torch.int8, 2)
+    _need(ksc, "ksc", torch.float16, 2)
+    _need(vsc, "vsc", torch.float16, 2)
+    n, D = k.shape
+    cap = kq.shape[0]
+    if tuple(v.shape) != (n, D):
+        raise ValueError("k and v must have the same shape")
+    if tuple(kq.shape) != (cap, D) or tuple(vq.shape) != (cap, D):
+        raise ValueError("kq and vq must be [cap][%d]" % D)
+    if tuple(ksc.shape) != (cap, D // GROUP) or tuple(vsc.shape) != (cap, D // GROUP):
+        raise ValueError("ksc and vsc must be [cap][%d]" % (D // GROUP))
+    _raise_on(lib().qsa_quant_append(_ptr(k), _ptr(v), n, D, _ptr(kq), _ptr(vq), _ptr(ksc), _ptr(vsc), cell0, cap,
+                                     _stream(stream)))

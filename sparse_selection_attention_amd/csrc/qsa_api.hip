@@ -298,4 +298,38 @@ qsa_status qsa_score(const float *q, const float *k, int32_t n_cells, int32_t po
     return launched(qsa::launch_score(a, static_cast<hipStream_t>(stream)), "qsa_score");
 }
 
+qsa_status qsa_quant_append(const float *k, const float *v, int32_t n_rows, int32_t D,
+                            int8_t *kq, int8_t *vq, void *ksc, void *vsc,
+                            int32_t cell0, int32_t n_cells_cap, void *stream)
+{
+    if (n_rows < 0 || cell0 < 0 || n_cells_cap < 0)
+        return fail(QSA_ERR_ARG, "qsa_quant_append: negative n_rows (%d), cell0 (%d) or n_cells_cap (%d)", n_rows,
+                    cell0, n_cells_cap);
+    if (D != qsa::kD)
+        return fail(QSA_ERR_UNSUPPORTED, "qsa_quant_append: head dim %d not implemented (only %d)", D, qsa::kD);
+    if ((int64_t)cell0 + n_rows > n_cells_cap)
+        return fail(QSA_ERR_ARG, "qsa_quant_append: cells %d .. %lld past the cache capacity %d", cell0,
+                    (long long)cell0 + n_rows - 1, n_cells_cap);
+    if (n_rows == 0)
+        return ok();
+    if (!k || !v || !kq || !vq || !ksc || !vsc)
+        return fail(QSA_ERR_ARG, "qsa_quant_append: NULL k, v, kq, vq, ksc or vsc");
+    if (!aligned(k, 16) || !aligned(v, 16) || !aligned(kq, 8) || !aligned(vq, 8) || !aligned(ksc, 8) ||
+        !aligned(vsc, 8))
+        return fail(QSA_ERR_ARG, "qsa_quant_append: misaligned pointer (k, v: 16 B; kq, vq, ksc, vsc: 8 B)");
+    qsa_status st = check_device();
+    if (st != QSA_OK)
+        return st;
+    qsa::QuantArgs a;
+    a.k = k;
+    a.v = v;
+    a.kq = kq;
+    a.vq = vq;
+    a.ksc = static_cast<uint16_t *>(ksc);
+    a.vsc = static_cast<uint16_t *>(vsc);
+    a.n_rows = n_rows;
+    a.cell0 = cell0;
+    return launched(qsa::launch_quant(a, static_cast<hipStream_t>(stream)), "qsa_quant_append");
+}
+
 } // extern "C"

@@ -47,6 +47,13 @@ struct ScoreArgs {
     int64_t row_stride;
 };
 
+struct QuantArgs {
+    const float *k, *v;       // [n_rows][D] fp32
+    int8_t *kq, *vq;          // [n_cells_cap][D]
+    uint16_t *ksc, *vsc;      // [n_cells_cap][D/32] fp16 bits
+    int32_t n_rows, cell0;    // rows land at cells cell0 .. cell0 + n_rows - 1
+};
+
 // Part workspace layout: o, then m, then l, each on a 256-byte boundary.
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 inline void part_layout(int64_t T, int64_t H, int64_t D, int64_t C,
@@ -64,5 +71,6 @@ hipError_t launch_attn(const AttnArgs &a, hipStream_t stream);
 hipError_t launch_attn_merge(const AttnArgs &a, hipStream_t stream);
 hipError_t launch_merge(const MergeArgs &a, hipStream_t stream);
 hipError_t launch_score(const ScoreArgs &a, hipStream_t stream);
+hipError_t launch_quant(const QuantArgs &a, hipStream_t stream);
 
 } // namespace qsa

@@ -34,6 +34,7 @@ _MASK = (1 << 64) - 1
 
 # tensor ids used to key the streams
 TID_Q, TID_KQ, TID_VQ, TID_KSC, TID_VSC, TID_SCORE_Q, TID_SCORE_K, TID_EDGE = range(8)
+TID_ROWS, TID_ROWS_MAG, TID_ROWS_INT = range(8, 11)
 
 HEAD_DIM = 128
 GROUP = 32          # one fp16 scale per 32 consecutive dims of a cached row
@@ -281,3 +282,53 @@ def score_case(T: int = 1984, pos0: int = 0, Hs: int = 1, seed: int = 5, D: int 
     k = normal(stream_key(seed, 0, TID_SCORE_K), n_cells * D).astype(np.float32).reshape(n_cells, D)
     return ScoreCase("score_T%d_p%d_h%d" % (T, pos0, Hs), T, pos0, Hs, D, n_cells, q, k,
                      np.float32(scale), np.float32(dead), row_stride)
+
+
+# ---------------------------------------------------------------------------
+# fp32 rows for the int8 cache writer
+
+
+ROW_KINDS = ("normal", "spread", "ties", "special")
+
+
+def cache_rows(n: int, seed: int = 5, kind: str = "normal", which: int = 0, D: int = HEAD_DIM) -> np.ndarray:
+    """fp32 rows [n][D] to be quantised into the cache; `which` (0 for K, 1 for V)
+    picks an independent stream.
+
+    normal   N(0, 1) values, the scale of normalised K and V rows;
+    spread   N(0, 1) times a per-group magnitude 10^U(-8, 6): fp16 scales from
+             zero (underflow) and subnormal up to ~3e4;
+    ties     per group an fp16 step s, one element 127 s and the others
+             (j + 1/2) s for integers |j| <= 126, so that x / s falls exactly
+             halfway between two codes;
+    special  zero and negative-zero groups, groups with one non-zero element,
+             subnormal-step groups and groups at the top of the fp16 range,
+             mixed with normal ones.
+    """
+    G = D // GROUP
+    layer = 100 + 10 * which + ROW_KINDS.index(kind)
+    z = normal(stream_key(seed, layer, TID_ROWS), n * D).reshape(n, G, GROUP)
+    u = uniform01(stream_key(seed, layer, TID_ROWS_MAG), n * G).reshape(n, G, 1)
+    if kind == "normal":
+        x = z
+    elif kind == "spread":
+        x = z * 10.0 ** (-8.0 + 14.0 * u)
+    elif kind == "ties":
+        step = (10.0 ** (-3.0 + 5.0 * u)).astype(np.float16).astype(np.float64)       # an fp16 step
+        j = (raw_u64(stream_key(seed, layer, TID_ROWS_INT), n * D) % np.uint64(253)).astype(np.int64) - 126
+        x = (j.reshape(n, G, GROUP) + 0.5) * step
+        x[:, :, 0] = 127.0 * step[:, :, 0]
+        x = x * np.where(z > 0, 1.0, -1.0)
+    elif kind == "special":
+        x = z.copy()
+        sel = (raw_u64(stream_key(seed, layer, TID_ROWS_INT), n * G) % np.uint64(6)).reshape(n, G)
+        x[sel == 0] = 0.0
+        x[sel == 1] = -0.0
+        one = x[sel == 2]
+        one[:, 1:] = 0.0
+        x[sel == 2] = one
+        x[sel == 3] *= 1e-6
+        x[sel == 4] *= 127.0 * 65504.0 / 5.0
+    else:
+        raise ValueError(kind)
+    return np.ascontiguousarray(x.reshape(n, D).astype(np.float32))

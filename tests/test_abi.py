@@ -24,8 +24,8 @@ def declared_symbols():
 def test_library_loads_and_exports_every_declared_symbol():
     L = qsa.lib()
     names = declared_symbols()
-    assert {"qsa_attn", "qsa_attn_merge", "qsa_merge", "qsa_score", "qsa_part_bytes", "qsa_part_offsets",
-            "qsa_last_error"} <= names
+    assert {"qsa_attn", "qsa_attn_merge", "qsa_merge", "qsa_score", "qsa_quant_append", "qsa_part_bytes",
+            "qsa_part_offsets", "qsa_last_error"} <= names
     for n in names:
         assert hasattr(L, n), n
 
@@ -207,3 +207,39 @@ def test_build_rejects_spilling_kernels():
     res = build.kernel_resources(text)
     assert res == {"kern_a": {"VGPRs": 120, "ScratchSize": 0, "Occupancy": 4},
                    "kern_b": {"VGPRs": 128, "ScratchSize": 60}}
+
+
+def quant(**kw):
+    a = dict(k=FAKE, v=FAKE, n_rows=10, D=128, kq=FAKE, vq=FAKE, ksc=FAKE, vsc=FAKE, cell0=5, cap=100)
+    a.update(kw)
+    P = ctypes.c_void_p
+    return qsa.lib().qsa_quant_append(P(a["k"]), P(a["v"]), a["n_rows"], a["D"], P(a["kq"]), P(a["vq"]),
+                                      P(a["ksc"]), P(a["vsc"]), a["cell0"], a["cap"], P(None))
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(n_rows=-1), qsa.QSA_ERR_ARG),
+    (dict(cell0=-1), qsa.QSA_ERR_ARG),
+    (dict(cap=-1), qsa.QSA_ERR_ARG),
+    (dict(D=64), qsa.QSA_ERR_UNSUPPORTED),
+    (dict(cell0=91), qsa.QSA_ERR_ARG),             # 91 + 10 > 100
+    (dict(cell0=2**31 - 5, cap=2**31 - 1), qsa.QSA_ERR_ARG),
+    (dict(k=None), qsa.QSA_ERR_ARG),
+    (dict(v=None), qsa.QSA_ERR_ARG),
+    (dict(kq=None), qsa.QSA_ERR_ARG),
+    (dict(vsc=None), qsa.QSA_ERR_ARG),
+    (dict(k=FAKE + 8), qsa.QSA_ERR_ARG),
+    (dict(v=FAKE + 4), qsa.QSA_ERR_ARG),
+    (dict(kq=FAKE + 4), qsa.QSA_ERR_ARG),
+    (dict(vq=FAKE + 2), qsa.QSA_ERR_ARG),
+    (dict(ksc=FAKE + 2), qsa.QSA_ERR_ARG),
+    (dict(vsc=FAKE + 4), qsa.QSA_ERR_ARG),
+])
+def test_quant_append_rejects_bad_arguments_on_host(kw, status):
+    assert quant(**kw) == status
+    assert qsa.qsa_last_error().startswith("qsa_quant_append")
+
+
+def test_quant_append_zero_rows_is_a_no_op():
+    assert quant(n_rows=0, k=None, kq=None, cell0=100) == qsa.QSA_OK
+    assert qsa.qsa_last_error() == ""
