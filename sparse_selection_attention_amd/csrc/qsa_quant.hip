@@ -12,11 +12,20 @@
 // half to even. The integer codes and the fp16 scale are decided in binary32,
 // so any implementation of the rule reproduces them bit for bit.
 //
-// Design on CDNA4: a streaming kernel. Each thread owns 8 consecutive
-// elements (two 16-byte loads), four threads one group, sixteen one row, so a
-// wave reads four 512-byte rows in one contiguous 2 KB sweep and writes four
-// 128-byte code rows. The group maximum is two lane exchanges. Row tasks run
-// over the K rows, then the V rows.
+// Design on CDNA4: a streaming kernel. Each thread owns 16 consecutive
+// elements (four 16-byte loads in flight), two threads one group, eight one
+// row, so a wave reads eight 512-byte rows in one contiguous 4 KB sweep and
+// writes eight 128-byte code rows. Row tasks run over the K rows, then the V
+// rows.
+//
+// The quotient x / s only has to decide an integer. Each element takes
+// q0 = x * rcp(s): the hardware reciprocal is within 1 ulp, so
+// |q0 - x/s| <= 256 * 1.5 * 2^-23 < 4.6e-5 over the range that is not clamped
+// (|x/s| < 256), and the correctly rounded quotient is within a further half
+// ulp (7.7e-6) of x/s. When q0 lies more than 2^-14 (6.1e-5) from every
+// half-integer, x/s and its correctly rounded binary32 value fall strictly on
+// the same side of the same half-integer, so rint(q0) is the code. The rare
+// lanes closer than that take the correctly rounded division.
 #include "qsa_internal.h"
 
 #include <hip/hip_fp16.h>
@@ -24,60 +33,76 @@
 namespace qsa {
 namespace {
 
-constexpr int kRowsPerBlock = 16;   // 256 threads, 16 per row
+typedef float f4v __attribute__((ext_vector_type(4)));
 
-__device__ inline float absmax8(float4 a, float4 b)
+constexpr int kRowsPerBlock = 32;   // 256 threads, 8 per row
+constexpr float kNear = 0.5f - 0x1p-14f;
+
+__device__ inline float absmax4(float4 a)
 {
-    return fmaxf(fmaxf(fmaxf(fabsf(a.x), fabsf(a.y)), fmaxf(fabsf(a.z), fabsf(a.w))),
-                 fmaxf(fmaxf(fabsf(b.x), fabsf(b.y)), fmaxf(fabsf(b.z), fabsf(b.w))));
+    return fmaxf(fmaxf(fabsf(a.x), fabsf(a.y)), fmaxf(fabsf(a.z), fabsf(a.w)));
 }
 
-__device__ inline uint32_t code_byte(float x, float s)
+// the code of one element: rint(x / s) clamped to +-127, decided as the
+// correctly rounded binary32 quotient would decide it (r = rcp(s), or 0 when
+// s is zero or infinite, which gives code 0)
+__device__ inline uint32_t code_byte(float x, float s, float r)
 {
-    float c = 0.0f;
-    if (s > 0.0f)
-        c = fminf(fmaxf(rintf(__fdiv_rn(x, s)), -127.0f), 127.0f);
+    const float q0 = x * r;
+    float c = rintf(q0);
+    if (fabsf(q0 - c) > kNear)                // within 2^-14 of a half-integer
+        c = rintf(__fdiv_rn(x, s));
+    c = __builtin_amdgcn_fmed3f(c, -127.0f, 127.0f);
     return (uint32_t)(int32_t)c & 0xffu;
 }
 
-__device__ inline uint32_t pack4(float4 x, float s)
+__device__ inline uint32_t pack4(float4 x, float s, float r)
 {
-    return code_byte(x.x, s) | (code_byte(x.y, s) << 8) | (code_byte(x.z, s) << 16) | (code_byte(x.w, s) << 24);
+    return code_byte(x.x, s, r) | (code_byte(x.y, s, r) << 8) | (code_byte(x.z, s, r) << 16) |
+           (code_byte(x.w, s, r) << 24);
 }
 
 __global__ __launch_bounds__(256) void quant_kernel(QuantArgs a)
 {
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int64_t task = (int64_t)blockIdx.x * kRowsPerBlock + (tid >> 4);
-    // all 16 threads of a row share `task`, so a row is wholly in or out
+    const int64_t task = (int64_t)blockIdx.x * kRowsPerBlock + (tid >> 3);
+    // all 8 threads of a row share `task`, so a row is wholly in or out
     const bool active = task < 2 * (int64_t)a.n_rows;
     const bool is_v = task >= a.n_rows;
     const int64_t r = is_v ? task - a.n_rows : task;
-    const int e0 = 8 * (tid & 15);
+    const int e0 = 16 * (tid & 7);
 
-    float4 x0 = make_float4(0.f, 0.f, 0.f, 0.f), x1 = x0;
+    float4 x[4];
     if (active) {
-        const float *src = (is_v ? a.v : a.k) + r * kD + e0;
-        x0 = *(const float4 *)src;
-        x1 = *(const float4 *)(src + 4);
+        const f4v *src = (const f4v *)((is_v ? a.v : a.k) + r * kD + e0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const f4v v = src[i];     // plain loads: nontemporal ones ran 35% slower here
+            x[i] = make_float4(v.x, v.y, v.z, v.w);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            x[i] = make_float4(0.f, 0.f, 0.f, 0.f);
     }
-    float amax = absmax8(x0, x1);
-    amax = fmaxf(amax, __shfl_xor(amax, 1, 64));        // the four threads of a group
-    amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
+    float amax = fmaxf(fmaxf(absmax4(x[0]), absmax4(x[1])), fmaxf(absmax4(x[2]), absmax4(x[3])));
+    amax = fmaxf(amax, __shfl_xor(amax, 1, 64));        // the two threads of a group
     const _Float16 s16 = (_Float16)__fdiv_rn(amax, 127.0f);    // binary32 quotient, then RNE to fp16
     const float s = (float)s16;
+    const float rcp = (s > 0.0f && s < INFINITY) ? __builtin_amdgcn_rcpf(s) : 0.0f;
 
-    const uint2 codes = make_uint2(pack4(x0, s), pack4(x1, s));
-    // the row's four scales, from its threads 0, 4, 8 and 12
+    const uint4 codes = make_uint4(pack4(x[0], s, rcp), pack4(x[1], s, rcp), pack4(x[2], s, rcp),
+                                   pack4(x[3], s, rcp));
+    // the row's four scales, from its threads 0, 2, 4 and 6
     const uint32_t sbits = (uint32_t)__builtin_bit_cast(uint16_t, s16);
-    const int row_lane = lane & ~15;
-    const uint32_t g0 = __shfl(sbits, row_lane + 0, 64), g1 = __shfl(sbits, row_lane + 4, 64);
-    const uint32_t g2 = __shfl(sbits, row_lane + 8, 64), g3 = __shfl(sbits, row_lane + 12, 64);
+    const int row_lane = lane & ~7;
+    const uint32_t g0 = __shfl(sbits, row_lane + 0, 64), g1 = __shfl(sbits, row_lane + 2, 64);
+    const uint32_t g2 = __shfl(sbits, row_lane + 4, 64), g3 = __shfl(sbits, row_lane + 6, 64);
     if (active) {
         const int64_t cell = (int64_t)a.cell0 + r;
-        *(uint2 *)((is_v ? a.vq : a.kq) + cell * kD + e0) = codes;
-        if ((tid & 15) == 0)
+        *(uint4 *)((is_v ? a.vq : a.kq) + cell * kD + e0) = codes;
+        if ((tid & 7) == 0)
             *(uint2 *)((is_v ? a.vsc : a.ksc) + cell * (kD / kGroup)) = make_uint2(g0 | (g1 << 16), g2 | (g3 << 16));
     }
 }

@@ -288,7 +288,7 @@ def score_case(T: int = 1984, pos0: int = 0, Hs: int = 1, seed: int = 5, D: int 
 # fp32 rows for the int8 cache writer
 
 
-ROW_KINDS = ("normal", "spread", "ties", "special")
+ROW_KINDS = ("normal", "spread", "ties", "near", "special")
 
 
 def cache_rows(n: int, seed: int = 5, kind: str = "normal", which: int = 0, D: int = HEAD_DIM) -> np.ndarray:
@@ -301,6 +301,8 @@ def cache_rows(n: int, seed: int = 5, kind: str = "normal", which: int = 0, D: i
     ties     per group an fp16 step s, one element 127 s and the others
              (j + 1/2) s for integers |j| <= 126, so that x / s falls exactly
              halfway between two codes;
+    near     like ties, but each element moved off the half-integer by a few
+             binary32 ulps or by 2^-15 .. 2^-12 of the step, either side;
     special  zero and negative-zero groups, groups with one non-zero element,
              subnormal-step groups and groups at the top of the fp16 range,
              mixed with normal ones.
@@ -317,6 +319,20 @@ def cache_rows(n: int, seed: int = 5, kind: str = "normal", which: int = 0, D: i
         step = (10.0 ** (-3.0 + 5.0 * u)).astype(np.float16).astype(np.float64)       # an fp16 step
         j = (raw_u64(stream_key(seed, layer, TID_ROWS_INT), n * D) % np.uint64(253)).astype(np.int64) - 126
         x = (j.reshape(n, G, GROUP) + 0.5) * step
+        x[:, :, 0] = 127.0 * step[:, :, 0]
+        x = x * np.where(z > 0, 1.0, -1.0)
+    elif kind == "near":
+        step = (10.0 ** (-3.0 + 5.0 * u)).astype(np.float16).astype(np.float64)
+        j = (raw_u64(stream_key(seed, layer, TID_ROWS_INT), n * D) % np.uint64(253)).astype(np.int64) - 126
+        pick = (raw_u64(stream_key(seed, layer, TID_ROWS_INT + 100), n * D) % np.uint64(12)).astype(np.int64)
+        sign = np.where(pick % 2 == 0, 1.0, -1.0)
+        frac = np.array([0, 0, 0, 0, 0, 0, 2.0 ** -15, 2.0 ** -15, 2.0 ** -14, 2.0 ** -14, 2.0 ** -12, 2.0 ** -12])[pick]
+        ulps = np.array([1, 1, 2, 2, 5, 5, 0, 0, 0, 0, 0, 0])[pick]
+        t = ((j + 0.5) + sign * frac).reshape(n, G, GROUP) * step
+        x = t.astype(np.float32)
+        # ulp steps away from the half-integer in binary32
+        x = np.where(ulps.reshape(n, G, GROUP) > 0,
+                     x + sign.reshape(n, G, GROUP) * ulps.reshape(n, G, GROUP) * np.spacing(x), x)
         x[:, :, 0] = 127.0 * step[:, :, 0]
         x = x * np.where(z > 0, 1.0, -1.0)
     elif kind == "special":
