@@ -29,6 +29,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 FP32_MFMA_PEAK_TFLOPS = 157.3
+FP16_MFMA_PEAK_TFLOPS = 2500.0
 
 
 def attn_bytes(ids, n_cells, T, H, D, C):
@@ -108,6 +109,7 @@ def main():
     ap.add_argument("--no-score", action="store_true", help="skip the companion score kernel")
     ap.add_argument("--no-fused", action="store_true", help="skip the single-dispatch attention + merge line")
     ap.add_argument("--no-quant", action="store_true", help="skip the int8 cache writer line")
+    ap.add_argument("--no-prompt", action="store_true", help="skip the prompt-start (shared tile) line")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="also run one device copy of this many MiB (for counter calibration)")
     args = ap.parse_args()
@@ -303,6 +305,54 @@ def main():
             "long_context_layer_gbs": b_layer / (us_layer * 1e-6) / 1e9,
             "prompt_1984_rows_us": us_prompt,
         }
+
+    if not args.no_prompt:
+        # prompt start: T=1984 at pos0=0, every causal cell (implicit rows). Blocks of
+        # (token, head) rows share each chunk's cells: QK and PV run as MFMA tiles.
+        pc = synth.prompt_start(implicit=True)
+        pe = synth.prompt_start(implicit=False)
+        PL = pc.layers[0]
+        pq, pkq, pvq, pks, pvs = up(PL.q), up(PL.kq), up(PL.vq), up(PL.ksc), up(PL.vsc)
+        pids = up(pe.ids)
+        pC = pc.n_chunks
+        ppart = qsa.alloc_part(pc.T, pc.H, D, pC, device=dev)
+        pout = torch.empty(pc.T, pc.H, D, dtype=torch.float16, device=dev)
+
+        def time_it(fn, reps=20):
+            for _ in range(3):
+                fn()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(reps):
+                fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) * 1e3 / reps
+
+        def two_kernel():
+            qsa.qsa_attn(pq, pkq, pvq, pks, pvs, None, 0, float(pc.scale), ppart, stream=stream)
+            qsa.qsa_merge(ppart, pC, pout, stream=stream)
+
+        us_fused = time_it(lambda: qsa.qsa_attn_merge(pq, pkq, pvq, pks, pvs, None, 0, float(pc.scale), pout,
+                                                      stream=stream))
+        us_two = time_it(two_kernel)
+        us_expl = time_it(lambda: qsa.qsa_attn_merge(pq, pkq, pvq, pks, pvs, pids, 0, float(pc.scale), pout,
+                                                     stream=stream))
+        # causal QK and PV: 2 x 2 x D flops per (token, head, selected cell)
+        pflops = 4.0 * D * pc.H * sum(pc.pos0 + t + 1 for t in range(pc.T))
+        tf = pflops / (us_fused * 1e-6) / 1e12
+        result["prompt_tiles"] = {
+            "workload": "prompt start: T=1984, pos0=0, 12 heads, every causal cell (implicit rows), one layer",
+            "entry": "qsa_attn_merge (ids NULL)",
+            "avg_us": us_fused,
+            "value": pc.T * pc.H / (us_fused * 1e-6),
+            "unit": "query-token*heads/s",
+            "roofline": {"bound": "mfma", "achieved": tf, "peak": FP16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": tf / FP16_MFMA_PEAK_TFLOPS},
+            "two_kernel_us": us_two,
+            "explicit_rows_per_token_kernel_us": us_expl,
+        }
+        del ppart
 
     if args.copy_calibration:
         # one elementwise kernel that reads n bytes and writes n bytes

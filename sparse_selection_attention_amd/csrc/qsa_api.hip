@@ -122,6 +122,8 @@ qsa_status check_attn(const char *fn, const void *q, const int8_t *kq, const int
         return fail(QSA_ERR_ARG, "%s: pos0 + T overflows int32", fn);
     if (n_cells > qsa::kMaxCells)
         return fail(QSA_ERR_UNSUPPORTED, "%s: at most %d cached rows (got %d)", fn, qsa::kMaxCells, n_cells);
+    if ((int64_t)T * H > INT32_MAX - 64)
+        return fail(QSA_ERR_ARG, "%s: T * H too large for one launch", fn);
     if (T == 0) {
         *noop = true;
         return QSA_OK;
@@ -188,6 +190,8 @@ qsa_status qsa_attn(const void *q, const int8_t *kq, const int8_t *vq,
     a.l = reinterpret_cast<float *>(pb + l_off);
     a.n_blocks = (int32_t)n_blocks;
     a.blocks_per_xcd = (int32_t)per_xcd;
+    if (!ids)   // implicit rows: blocks of (token, head) rows share each chunk's cells
+        return launched(qsa::launch_attn_tile(a, static_cast<hipStream_t>(stream)), "qsa_attn");
     return launched(qsa::launch_attn(a, static_cast<hipStream_t>(stream)), "qsa_attn");
 }
 
@@ -215,6 +219,8 @@ qsa_status qsa_attn_merge(const void *q, const int8_t *kq, const int8_t *vq,
     a.out = static_cast<_Float16 *>(out);
     a.n_blocks = T;
     a.blocks_per_xcd = (T + 7) / 8;
+    if (!ids)   // implicit rows: blocks of (token, head) rows share each chunk's cells
+        return launched(qsa::launch_attn_merge_tile(a, static_cast<hipStream_t>(stream)), "qsa_attn_merge");
     return launched(qsa::launch_attn_merge(a, static_cast<hipStream_t>(stream)), "qsa_attn_merge");
 }
 

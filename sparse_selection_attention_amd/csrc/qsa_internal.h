@@ -69,6 +69,9 @@ inline void part_layout(int64_t T, int64_t H, int64_t D, int64_t C,
 
 hipError_t launch_attn(const AttnArgs &a, hipStream_t stream);
 hipError_t launch_attn_merge(const AttnArgs &a, hipStream_t stream);
+// implicit rows (ids == nullptr): token blocks share each chunk's cells
+hipError_t launch_attn_tile(const AttnArgs &a, hipStream_t stream);
+hipError_t launch_attn_merge_tile(const AttnArgs &a, hipStream_t stream);
 hipError_t launch_merge(const MergeArgs &a, hipStream_t stream);
 hipError_t launch_score(const ScoreArgs &a, hipStream_t stream);
 hipError_t launch_quant(const QuantArgs &a, hipStream_t stream);

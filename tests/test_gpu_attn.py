@@ -46,17 +46,23 @@ def test_prompt_start_explicit():
     _print("prompt", check_attn_case(synth.prompt_start(), n_sample=16))
 
 
-def test_prompt_start_implicit_rows_match_explicit_bitwise():
+def test_prompt_start_implicit_rows_match_explicit():
+    """Implicit rows run on the shared-tile kernel, explicit ones on the per-token
+    kernel: the same selection (empty records bit for bit), the same outputs and
+    records within tolerance, on every token."""
     case = synth.prompt_start()
     L = case.layers[0]
     a = run_attn(L, case.ids, case.pos0, case.scale)
     b = run_attn(L, None, case.pos0, case.scale, implicit=True)
     assert a[4] == b[4]
-    assert np.array_equal(a[0].view(np.uint16), b[0].view(np.uint16))
-    assert np.array_equal(a[2].view(np.uint32), b[2].view(np.uint32))
-    assert np.array_equal(a[3].view(np.uint32), b[3].view(np.uint32))
-    valid = ~np.isinf(a[2])                      # o is written only for non-empty chunks
-    assert np.array_equal(a[1].view(np.uint32)[valid], b[1].view(np.uint32)[valid])
+    empty_a, empty_b = np.isinf(a[2]), np.isinf(b[2])
+    assert np.array_equal(empty_a, empty_b)
+    assert np.all(b[2][empty_b] == -np.inf) and np.all(b[3][empty_b].view(np.uint32) == 0)
+    for t in range(case.T):
+        check_out(b[0][t], a[0][t].astype(np.float64), "implicit vs explicit t=%d" % t)
+    ne = ~empty_a
+    assert np.all(np.abs(a[2][ne] - b[2][ne]) <= 1e-4 * np.maximum(1.0, np.abs(a[2][ne])))
+    assert np.all(np.abs(a[3][ne] - b[3][ne]) <= 2e-3 * a[3][ne])
 
 
 def test_prompt_start_implicit_vs_oracle():
