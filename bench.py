@@ -178,7 +178,7 @@ def main():
     merge_avg_s = float(np.mean(merge_ms)) * 1e-3
     attn_gbs = a_bytes / attn_avg_s / 1e9
     step_bytes = args.layers * (a_bytes + m_bytes)
-    traffic = read_traffic(os.path.join(ROOT, "profiles", "qsa_attn_long_counters.md"),
+    traffic = read_traffic(os.path.join(ROOT, "profiles", "qsa_kernels_hbm_counters_bench_workloads.md"),
                            os.path.join(ROOT, "sparse_selection_attention_amd", "csrc", "qsa_attn.hip"))
 
     result = {
