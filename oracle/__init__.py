@@ -24,7 +24,7 @@ _lib = None
 
 def build() -> str:
     """Compile the oracle with gcc: -O2, no contraction, no fast-math."""
-    cmd = ["gcc", "-std=c99", "-O2", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared",
+    cmd = ["gcc", "-std=c11", "-O2", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared",
            "-Wall", "-Werror", _SRC, "-o", LIB_PATH + ".tmp", "-lm"]
     _sp.run(cmd, check=True)
     _os.replace(LIB_PATH + ".tmp", LIB_PATH)
@@ -53,6 +53,8 @@ def lib():
         L.qso_score.restype = _ct.c_int
         L.qso_quant_rows.argtypes = [P, i32, i32, P, P]
         L.qso_quant_rows.restype = _ct.c_int
+        L.qso_select.argtypes = [P, _ct.c_int64, i32, i32, i32, P, i32, i32, i32]
+        L.qso_select.restype = _ct.c_int
         _lib = L
     return _lib
 
@@ -177,3 +179,18 @@ def quant_rows(x):
     if lib().qso_quant_rows(_ptr(x), n, D, _ptr(codes), _ptr(scales)) != 0:
         raise ValueError("qso_quant_rows: bad arguments")
     return codes, scales
+
+
+def select(scores, pos0, K, ids_stride, t_range=None, threads=1):
+    """Top-K causal cell ids per row (qso_select): int32 [T][ids_stride], -1 padded."""
+    scores = _np.ascontiguousarray(scores, dtype=_np.float32)
+    T, row_stride = scores.shape
+    ids = _np.full((T, ids_stride), -2, dtype=_np.int32)
+    t0, t1 = (0, T) if t_range is None else t_range
+
+    def run(r):
+        if lib().qso_select(_ptr(scores), row_stride, pos0, T, K, _ptr(ids), ids_stride, r[0], r[1]) != 0:
+            raise ValueError("qso_select rejected the arguments")
+
+    _run_ranges(run, _ranges(t0, t1, threads))
+    return ids

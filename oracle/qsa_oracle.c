@@ -57,10 +57,19 @@
  *    binary32: with 53 >= 2 * 24 + 2 bits that double rounding gives the
  *    correctly rounded binary32 quotient (Figueroa, "When is double rounding
  *    innocuous?", 1995).
+ *  qso_select -- the ids a query row attends over, chosen from its causal
+ *    scores. The pages only say that the selected ids are unique causal cells
+ *    ("round 11 track b: qsa attention and score", section "boundaries and
+ *    provenance") and never print a rule; the reading taken is top-K: row t
+ *    (p = pos0 + t) takes the min(K, p + 1) cells c <= p with the largest
+ *    scores[t][c], equal scores (-0 equal to +0) going to the smaller cell
+ *    index, written in ascending cell order and padded with -1 to ids_stride.
+ *    Scores must not be NaN.
  */
 #include <math.h>
 #include <stddef.h>
 #include <stdint.h>
+#include <stdlib.h>
 
 #define QSO_GROUP 32
 #define QSO_CHUNK 64
@@ -310,5 +319,59 @@ int qso_quant_rows(const float *x, int32_t n_rows, int32_t D, int8_t *codes, uin
             }
         }
     }
+    return 0;
+}
+
+/* ---- top-K selection of causal cells ------------------------------------------ */
+
+/* qsort takes no context argument: the row being sorted is passed through this
+ * per-call pointer (the Python wrapper runs rows in parallel threads, so it is
+ * thread-local). */
+static _Thread_local const float *sel_row;
+
+static int by_score_then_index(const void *pa, const void *pb)
+{
+    const int32_t a = *(const int32_t *)pa, b = *(const int32_t *)pb;
+    const float sa = sel_row[a], sb = sel_row[b];
+    if (sa > sb)
+        return -1;
+    if (sa < sb)
+        return 1;
+    return (a > b) - (a < b);
+}
+
+static int by_index(const void *pa, const void *pb)
+{
+    const int32_t a = *(const int32_t *)pa, b = *(const int32_t *)pb;
+    return (a > b) - (a < b);
+}
+
+int qso_select(const float *scores, int64_t row_stride, int32_t pos0, int32_t T, int32_t K,
+               int32_t *ids, int32_t ids_stride, int32_t t_begin, int32_t t_end)
+{
+    if (T < 0 || pos0 < 0 || K < 1 || row_stride < (int64_t)pos0 + T || t_begin < 0 || t_end > T)
+        return 1;
+    int32_t *order = (int32_t *)malloc(sizeof(int32_t) * ((size_t)pos0 + T + 1));
+    if (!order)
+        return 2;
+    for (int32_t t = t_begin; t < t_end; ++t) {
+        const int32_t n = pos0 + t + 1;               /* cells 0 .. p */
+        const int32_t take = n < K ? n : K;
+        if (take > ids_stride) {
+            free(order);
+            return 1;
+        }
+        for (int32_t c = 0; c < n; ++c)
+            order[c] = c;
+        if (n > K) {
+            sel_row = scores + (int64_t)t * row_stride;
+            qsort(order, (size_t)n, sizeof(int32_t), by_score_then_index);
+            qsort(order, (size_t)take, sizeof(int32_t), by_index);
+        }
+        int32_t *row = ids + (int64_t)t * ids_stride;
+        for (int32_t j = 0; j < ids_stride; ++j)
+            row[j] = j < take ? order[j] : -1;
+    }
+    free(order);
     return 0;
 }
