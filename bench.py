@@ -10,8 +10,9 @@ one stream, with every input resident in HBM before the timed region.
 Prints one JSON line: query-token*heads per second, achieved algorithmic GB/s,
 the roofline of the dominant kernel (qsa_attn) measured with HIP events inside
 the timed region, the single-dispatch attention + merge, the companion
-causal-score kernel, the int8 cache writer, and the CPU oracle timed on a
-bounded sample on this host's cores.
+causal-score kernel, the selection producer on its output, the int8 cache
+writer, the shared-tile prompt path, and the CPU oracle timed on a bounded
+sample on this host's cores.
 """
 from __future__ import annotations
 
@@ -267,7 +268,27 @@ def main():
             "roofline": {"bound": "mfma", "achieved": flops / (us * 1e-6) / 1e12, "peak": FP32_MFMA_PEAK_TFLOPS,
                          "unit": "TFLOP/s", "frac": flops / (us * 1e-6) / 1e12 / FP32_MFMA_PEAK_TFLOPS},
         }
-        del scores
+        # selection producer on those scores: K = 2051 ids per row (the long-context selection size)
+        K_sel = 2051
+        sel_stride = 64 * ((K_sel + 63) // 64)
+        sel_ids = torch.empty(T, sel_stride, dtype=torch.int32, device=dev)
+        for _ in range(2):
+            qsa.qsa_select(scores, sc.pos0, K_sel, sel_ids, stream=stream)
+        e0.record(stream)
+        for _ in range(reps):
+            qsa.qsa_select(scores, sc.pos0, K_sel, sel_ids, stream=stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us_sel = e0.elapsed_time(e1) * 1e3 / reps
+        sel_bytes = 4.0 * sum(sc.pos0 + t + 1 for t in range(T)) + 4.0 * T * sel_stride
+        result["selection_producer"] = {
+            "entry": "qsa_select",
+            "workload": "top-2051 of the causal scores of 1984 rows at pos0=30000 (qsa_score's output)",
+            "avg_us": us_sel,
+            "roofline": {"bound": "hbm", "achieved": sel_bytes / (us_sel * 1e-6) / 1e9, "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": sel_bytes / (us_sel * 1e-6) / 1e9 / HBM_PEAK_GBS},
+        }
+        del scores, sel_ids
 
     if not args.no_quant:
         # int8 cache writer: fp32 K and V rows -> int8 rows + per-32 fp16 scales.

@@ -182,6 +182,26 @@ QSA_API qsa_status qsa_quant_append(const float *k, const float *v, int32_t n_ro
                             int8_t *kq, int8_t *vq, void *ksc, void *vsc,
                             int32_t cell0, int32_t n_cells_cap, void *stream);
 
+/*
+ * qsa_select -- the ids each query row attends over, chosen from its causal
+ * scores (the selection step before qsa_attn).
+ *
+ * The pages say that a row's selected ids are unique causal cells ("round 11
+ * track b: qsa attention and score", section "boundaries and provenance") but
+ * do not print how they are chosen. The rule taken is top-K: row t
+ * (p = pos0 + t) selects the min(K, p + 1) cells c <= p with the largest
+ * scores[t][c]; equal scores (-0 and +0 are equal) go to the smaller cell.
+ * ids[t] receives them in ascending cell order, then -1 up to ids_stride.
+ * Only cells 0 .. p of each score row are read. Scores must not be NaN.
+ *
+ * scores      fp32 [T][row_stride] (e.g. qsa_score's output); row_stride >= pos0 + T
+ * ids         int32 [T][ids_stride]; ids_stride a multiple of 64 holding
+ *             min(K, pos0 + T) ids, so the rows feed qsa_attn directly
+ * This build supports pos0 + T <= 32768 (QSA_ERR_UNSUPPORTED beyond).
+ */
+QSA_API qsa_status qsa_select(const float *scores, int64_t row_stride, int32_t pos0, int32_t T, int32_t K,
+                      int32_t *ids, int32_t ids_stride, void *stream);
+
 /* Bytes of the `part` workspace for T tokens, H heads, head dim D, n_chunks chunks. */
 QSA_API size_t qsa_part_bytes(int32_t T, int32_t H, int32_t D, int32_t n_chunks);
 

@@ -16,7 +16,8 @@ import torch
 
 __all__ = [
     "QsaError", "CHUNK", "GROUP", "HEAD_DIM",
-    "qsa_attn", "qsa_attn_merge", "qsa_merge", "qsa_score", "qsa_quant_append", "qsa_part_bytes", "qsa_part_offsets",
+    "qsa_attn", "qsa_attn_merge", "qsa_merge", "qsa_score", "qsa_quant_append", "qsa_select", "qsa_part_bytes",
+    "qsa_part_offsets",
     "qsa_last_error",
     "alloc_part", "part_views", "chunk_count", "lib", "LIB_PATH",
 ]
@@ -57,6 +58,8 @@ def lib() -> ctypes.CDLL:
         L.qsa_score.restype = ctypes.c_int
         L.qsa_quant_append.argtypes = [P, P, i32, i32, P, P, P, P, i32, i32, P]
         L.qsa_quant_append.restype = ctypes.c_int
+        L.qsa_select.argtypes = [P, i64, i32, i32, i32, P, i32, P]
+        L.qsa_select.restype = ctypes.c_int
         L.qsa_part_bytes.argtypes = [i32, i32, i32, i32]
         L.qsa_part_bytes.restype = ctypes.c_size_t
         L.qsa_part_offsets.argtypes = [i32, i32, i32, i32, ctypes.POINTER(ctypes.c_size_t),
@@ -230,3 +233,14 @@ def qsa_quant_append(k: torch.Tensor, v: torch.Tensor, kq: torch.Tensor, vq: tor
         raise ValueError("ksc and vsc must be [cap][%d]" % (D // GROUP))
     _raise_on(lib().qsa_quant_append(_ptr(k), _ptr(v), n, D, _ptr(kq), _ptr(vq), _ptr(ksc), _ptr(vsc), cell0, cap,
                                      _stream(stream)))
+
+
+def qsa_select(scores: torch.Tensor, pos0: int, K: int, ids: torch.Tensor, stream=None) -> None:
+    """Top-K causal cell ids per row of scores (fp32 [T][row_stride]) into ids
+    (int32 [T][ids_stride]), ascending, -1 padded."""
+    _need(scores, "scores", torch.float32, 2)
+    _need(ids, "ids", torch.int32, 2)
+    T, row_stride = scores.shape
+    if ids.shape[0] != T:
+        raise ValueError("ids must have T rows")
+    _raise_on(lib().qsa_select(_ptr(scores), row_stride, pos0, T, K, _ptr(ids), ids.shape[1], _stream(stream)))

@@ -338,4 +338,41 @@ qsa_status qsa_quant_append(const float *k, const float *v, int32_t n_rows, int3
     return launched(qsa::launch_quant(a, static_cast<hipStream_t>(stream)), "qsa_quant_append");
 }
 
+qsa_status qsa_select(const float *scores, int64_t row_stride, int32_t pos0, int32_t T, int32_t K,
+                      int32_t *ids, int32_t ids_stride, void *stream)
+{
+    if (T < 0 || pos0 < 0)
+        return fail(QSA_ERR_ARG, "qsa_select: negative T (%d) or pos0 (%d)", T, pos0);
+    if (K < 1)
+        return fail(QSA_ERR_ARG, "qsa_select: K must be >= 1 (got %d)", K);
+    if ((int64_t)pos0 + T > qsa::kMaxSelectCells)
+        return fail(QSA_ERR_UNSUPPORTED, "qsa_select: rows of at most %d cells (pos0 + T = %lld)",
+                    qsa::kMaxSelectCells, (long long)pos0 + T);
+    if (row_stride < (int64_t)pos0 + T)
+        return fail(QSA_ERR_ARG, "qsa_select: row_stride (%lld) < pos0 + T (%lld)", (long long)row_stride,
+                    (long long)pos0 + T);
+    const int64_t longest = (int64_t)pos0 + T < K ? (int64_t)pos0 + T : K;
+    if (ids_stride <= 0 || ids_stride % QSA_CHUNK != 0 || ids_stride < longest)
+        return fail(QSA_ERR_ARG, "qsa_select: ids_stride (%d) must be a positive multiple of %d holding min(K, pos0 + T) = %lld ids",
+                    ids_stride, QSA_CHUNK, (long long)longest);
+    if (T == 0)
+        return ok();
+    if (!scores || !ids)
+        return fail(QSA_ERR_ARG, "qsa_select: NULL scores or ids");
+    if (!aligned(scores, 4) || !aligned(ids, 4))
+        return fail(QSA_ERR_ARG, "qsa_select: misaligned pointer (scores, ids: 4 B)");
+    qsa_status st = check_device();
+    if (st != QSA_OK)
+        return st;
+    qsa::SelectArgs a;
+    a.scores = scores;
+    a.row_stride = row_stride;
+    a.pos0 = pos0;
+    a.T = T;
+    a.K = K;
+    a.ids = ids;
+    a.ids_stride = ids_stride;
+    return launched(qsa::launch_select(a, static_cast<hipStream_t>(stream)), "qsa_select");
+}
+
 } // extern "C"

@@ -54,6 +54,15 @@ struct QuantArgs {
     int32_t n_rows, cell0;    // rows land at cells cell0 .. cell0 + n_rows - 1
 };
 
+struct SelectArgs {
+    const float *scores;      // [T][row_stride]
+    int64_t row_stride;
+    int32_t pos0, T, K;
+    int32_t *ids;             // [T][ids_stride]
+    int32_t ids_stride;
+};
+constexpr int kMaxSelectCells = 1 << 15;   // cells per row the selection kernel holds in registers
+
 // Part workspace layout: o, then m, then l, each on a 256-byte boundary.
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 inline void part_layout(int64_t T, int64_t H, int64_t D, int64_t C,
@@ -75,5 +84,6 @@ hipError_t launch_attn_merge_tile(const AttnArgs &a, hipStream_t stream);
 hipError_t launch_merge(const MergeArgs &a, hipStream_t stream);
 hipError_t launch_score(const ScoreArgs &a, hipStream_t stream);
 hipError_t launch_quant(const QuantArgs &a, hipStream_t stream);
+hipError_t launch_select(const SelectArgs &a, hipStream_t stream);
 
 } // namespace qsa

@@ -35,6 +35,7 @@ _MASK = (1 << 64) - 1
 # tensor ids used to key the streams
 TID_Q, TID_KQ, TID_VQ, TID_KSC, TID_VSC, TID_SCORE_Q, TID_SCORE_K, TID_EDGE = range(8)
 TID_ROWS, TID_ROWS_MAG, TID_ROWS_INT = range(8, 11)
+TID_SEL, TID_SEL_INT = range(11, 13)
 
 HEAD_DIM = 128
 GROUP = 32          # one fp16 scale per 32 consecutive dims of a cached row
@@ -348,3 +349,49 @@ def cache_rows(n: int, seed: int = 5, kind: str = "normal", which: int = 0, D: i
     else:
         raise ValueError(kind)
     return np.ascontiguousarray(x.reshape(n, D).astype(np.float32))
+
+
+# ---------------------------------------------------------------------------
+# score rows for the selection producer
+
+
+SCORE_KINDS = ("normal", "ties", "special")
+
+
+def select_scores(T: int, pos0: int, seed: int = 5, kind: str = "normal", row_stride: Optional[int] = None) -> np.ndarray:
+    """fp32 score rows [T][row_stride] (row_stride >= pos0 + T) to select from.
+
+    normal   N(0, 1) values;
+    ties     values on a grid of quarters in [-5, 5] (many equal scores), with
+             signed zeros;
+    special  N(0, 1) with +-inf, +-0 and large runs of one repeated value.
+    Cells past each row's causal edge hold 3e38, larger than every causal
+    score, so a selection that read past the edge would pick them.
+    """
+    if row_stride is None:
+        row_stride = pos0 + T
+    n = T * row_stride
+    z = normal(stream_key(seed, 200 + SCORE_KINDS.index(kind), TID_SEL), n).reshape(T, row_stride)
+    if kind == "normal":
+        x = z
+    elif kind == "ties":
+        r = raw_u64(stream_key(seed, 200 + SCORE_KINDS.index(kind), TID_SEL_INT), n).reshape(T, row_stride)
+        x = ((r % np.uint64(41)).astype(np.int64) - 20) / 4.0
+        x = np.where((r >> np.uint64(40)) % np.uint64(16) == 0, np.where(z > 0, 0.0, -0.0), x)
+    elif kind == "special":
+        r = raw_u64(stream_key(seed, 200 + SCORE_KINDS.index(kind), TID_SEL_INT), n).reshape(T, row_stride)
+        sel = (r % np.uint64(50)).astype(np.int64)
+        x = z.copy()
+        x[sel == 0] = np.inf
+        x[sel == 1] = -np.inf
+        x[sel == 2] = 0.0
+        x[sel == 3] = -0.0
+        x[(sel >= 4) & (sel < 12)] = 1.25
+    else:
+        raise ValueError(kind)
+    x = x.astype(np.float32)
+    # beyond the causal edge: a huge value, so reading it would change the selection
+    cols = np.arange(row_stride)[None, :]
+    p = pos0 + np.arange(T)[:, None]
+    x[cols > p] = np.float32(3e38)
+    return np.ascontiguousarray(x)

@@ -24,8 +24,8 @@ def declared_symbols():
 def test_library_loads_and_exports_every_declared_symbol():
     L = qsa.lib()
     names = declared_symbols()
-    assert {"qsa_attn", "qsa_attn_merge", "qsa_merge", "qsa_score", "qsa_quant_append", "qsa_part_bytes",
-            "qsa_part_offsets", "qsa_last_error"} <= names
+    assert {"qsa_attn", "qsa_attn_merge", "qsa_merge", "qsa_score", "qsa_quant_append", "qsa_select",
+            "qsa_part_bytes", "qsa_part_offsets", "qsa_last_error"} <= names
     for n in names:
         assert hasattr(L, n), n
 
@@ -243,3 +243,34 @@ def test_quant_append_rejects_bad_arguments_on_host(kw, status):
 def test_quant_append_zero_rows_is_a_no_op():
     assert quant(n_rows=0, k=None, kq=None, cell0=100) == qsa.QSA_OK
     assert qsa.qsa_last_error() == ""
+
+
+def select(**kw):
+    a = dict(scores=FAKE, row_stride=100, pos0=50, T=10, K=20, ids=FAKE, ids_stride=64)
+    a.update(kw)
+    P = ctypes.c_void_p
+    return qsa.lib().qsa_select(P(a["scores"]), a["row_stride"], a["pos0"], a["T"], a["K"], P(a["ids"]),
+                                a["ids_stride"], P(None))
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(T=-1), qsa.QSA_ERR_ARG),
+    (dict(pos0=-1), qsa.QSA_ERR_ARG),
+    (dict(K=0), qsa.QSA_ERR_ARG),
+    (dict(row_stride=59), qsa.QSA_ERR_ARG),          # < pos0 + T
+    (dict(ids_stride=0), qsa.QSA_ERR_ARG),
+    (dict(ids_stride=32), qsa.QSA_ERR_ARG),          # not a multiple of 64
+    (dict(K=100, pos0=100, row_stride=200, ids_stride=64), qsa.QSA_ERR_ARG),   # min(K, pos0 + T) = 100 > 64
+    (dict(pos0=32760, T=10, row_stride=40000), qsa.QSA_ERR_UNSUPPORTED),
+    (dict(scores=None), qsa.QSA_ERR_ARG),
+    (dict(ids=None), qsa.QSA_ERR_ARG),
+    (dict(scores=FAKE + 2), qsa.QSA_ERR_ARG),
+    (dict(ids=FAKE + 1), qsa.QSA_ERR_ARG),
+])
+def test_select_rejects_bad_arguments_on_host(kw, status):
+    assert select(**kw) == status
+    assert qsa.qsa_last_error().startswith("qsa_select")
+
+
+def test_select_zero_rows_is_a_no_op():
+    assert select(T=0, scores=None, ids=None) == qsa.QSA_OK
