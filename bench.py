@@ -111,6 +111,7 @@ def main():
     ap.add_argument("--no-fused", action="store_true", help="skip the single-dispatch attention + merge line")
     ap.add_argument("--no-quant", action="store_true", help="skip the int8 cache writer line")
     ap.add_argument("--no-prompt", action="store_true", help="skip the prompt-start (shared tile) line")
+    ap.add_argument("--no-decode", action="store_true", help="skip the decode-window latency line")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="also run one device copy of this many MiB (for counter calibration)")
     args = ap.parse_args()
@@ -374,6 +375,43 @@ def main():
             "explicit_rows_per_token_kernel_us": us_expl,
         }
         del ppart
+
+    if not args.no_decode:
+        # decode: ntok tokens at pos0=3000 over the 321-cell window (64 sink + 256
+        # local + current), 12 heads: latency of one call, fused and two-kernel
+        lat = {}
+        for ntok in (1, 2, 4, 8):
+            mc = synth.mtp(ntok)
+            ML = mc.layers[0]
+            mq, mkq, mvq, mks, mvs = up(ML.q), up(ML.kq), up(ML.vq), up(ML.ksc), up(ML.vsc)
+            mids = up(mc.ids)
+            mout = torch.empty(ntok, mc.H, D, dtype=torch.float16, device=dev)
+            mpart = qsa.alloc_part(ntok, mc.H, D, mc.n_chunks, device=dev)
+
+            def fused():
+                qsa.qsa_attn_merge(mq, mkq, mvq, mks, mvs, mids, mc.pos0, float(mc.scale), mout, stream=stream)
+
+            def two():
+                qsa.qsa_attn(mq, mkq, mvq, mks, mvs, mids, mc.pos0, float(mc.scale), mpart, stream=stream)
+                qsa.qsa_merge(mpart, mc.n_chunks, mout, stream=stream)
+
+            row = {}
+            for name, fn in (("fused_us", fused), ("two_kernel_us", two)):
+                for _ in range(5):
+                    fn()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                for _ in range(100):
+                    fn()
+                e1.record(stream)
+                torch.cuda.synchronize()
+                row[name] = e0.elapsed_time(e1) * 1e3 / 100
+            lat["ntok_%d" % ntok] = row
+        result["decode_latency"] = {
+            "workload": "decode window: ntok tokens at pos0=3000, 321 cells (64 sink + 256 local + current), 12 heads, "
+                        "back-to-back calls on one stream",
+            **lat,
+        }
 
     if args.copy_calibration:
         # one elementwise kernel that reads n bytes and writes n bytes
