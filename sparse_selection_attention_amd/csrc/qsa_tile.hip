@@ -33,7 +33,11 @@
 //     row block are split over workgroups of at most 8 chunks each, so the
 //     long rows of late tokens do not serialise; fused
 //     (qsa_attn_merge): a running max, denominator and output per row,
-//     rescaled as each chunk's max arrives, divided once at the end.
+//     rescaled as each chunk's max arrives, divided once at the end. A fused
+//     workgroup holds three such groups of four waves, each with its own LDS
+//     tiles, walking every third chunk of the same rows; their states are
+//     combined through LDS at the end (the same max-first rule), so the
+//     longest row block walks a third as many chunks in sequence.
 // The V scales of a chunk whose largest scale reaches 2^9 are multiplied by a
 // common power of two first (vq * vsc could leave fp16 range), taken back out
 // exactly on p. Workgroups start with the heaviest row blocks (the last
@@ -57,6 +61,8 @@ constexpr int kLKs = kLVl + kD * kChunk * 2;   // K scales fp16 [64 cells][4]
 constexpr int kLE = kLKs + kChunk * 8;         // int[4]: largest V-scale exponent seen by each wave
 constexpr int kTileLds = kLE + 16;
 constexpr int kSplit = 8;                      // chunks per workgroup in the chunk-record kernel
+constexpr int kFusedGroups = 3;                // groups of four waves per fused workgroup
+static_assert(kTileLds % 16 == 0 && 4 * 64 * 36 * 4 <= kTileLds, "group state must fit a group's tiles");
 
 // K tile: cell c's logical granule gi (dims 8gi .. 8gi+7) at gi ^ (c & 15)
 __device__ inline int tk_offset(int c, int gi) { return kLK + c * 256 + ((gi ^ (c & 15)) << 4); }
@@ -183,13 +189,18 @@ __device__ inline void stage_tiles(uint8_t *lds, int tid, const Raw &R, uint32_t
     }
 }
 
-template <bool kFused>
-__global__ __launch_bounds__(kTileThreads) void attn_tile_kernel(AttnArgs a, int n_parts)
+// G groups of four waves share a workgroup's rows: group gi walks chunks
+// k_lo + gi, k_lo + gi + G, ... with LDS tiles of its own, and the groups'
+// running (max, denominator, output) are combined at the end (fused kernel).
+template <bool kFused, int G>
+__global__ __launch_bounds__(kTileThreads * G) void attn_tile_kernel(AttnArgs a, int n_parts)
 {
-    __shared__ __align__(16) uint8_t lds[kTileLds];
+    __shared__ __align__(16) uint8_t lds_all[G * kTileLds];
+    const int gi = (int)threadIdx.x / kTileThreads;
+    uint8_t *lds = lds_all + gi * kTileLds;
     int *s_e = (int *)(lds + kLE);
 
-    const int tid = threadIdx.x;
+    const int tid = (int)threadIdx.x % kTileThreads;    // thread within the group
     const int lane = tid & 63, w = tid >> 6;
     const int j = lane >> 4, c16 = lane & 15;
     const int n_rows = a.T * a.H;
@@ -220,8 +231,10 @@ __global__ __launch_bounds__(kTileThreads) void attn_tile_kernel(AttnArgs a, int
         qop[g] = row_ok ? *(const half8 *)(a.q + (int64_t)row * kD + 32 * g + 8 * j) : (half8)(_Float16)0.0f;
 
     Raw R;
-    if (k_lo <= k_end)
-        load_raw(a, k_lo * kChunk, tid, R);
+    const int n_walk = k_end - k_lo + 1;
+    const int n_iter = n_walk > 0 ? (n_walk + G - 1) / G : 0;
+    if (k_lo + gi <= k_end)
+        load_raw(a, (k_lo + gi) * kChunk, tid, R);
 
     float Mrun = -INFINITY, Lrun = 0.0f;
     floatx4 O[8];
@@ -229,23 +242,28 @@ __global__ __launch_bounds__(kTileThreads) void attn_tile_kernel(AttnArgs a, int
     for (int n = 0; n < 8; ++n)
         O[n] = (floatx4){0.f, 0.f, 0.f, 0.f};
 
-    for (int k = k_lo; k <= k_end; ++k) {
+    for (int it = 0; it < n_iter; ++it) {
+        const int k = k_lo + gi + it * G;
+        const bool act = k <= k_end;            // uniform over the group: groups past the end idle
         const int c0 = k * kChunk;
         // every read issued so far (q, this chunk's rows) has landed: stated
         // here so that the contractions below wait on none of the next
         // chunk's reads, which are issued before them
         __builtin_amdgcn_s_waitcnt(0);
-        {
+        if (act) {
             const uint32_t ew = wave_max_exponent(vs_exponent(R));
             if (lane == 0)
                 s_e[w] = (int)ew;
         }
         __syncthreads();                        // the previous chunk's tiles are no longer read
         const uint32_t e = (uint32_t)max(max(s_e[0], s_e[1]), max(s_e[2], s_e[3]));
-        stage_tiles(lds, tid, R, e);
+        if (act)
+            stage_tiles(lds, tid, R, e);
         __syncthreads();                        // the chunk's tiles are in place
-        if (k < k_end)
-            load_raw(a, c0 + kChunk, tid, R);   // in flight during this chunk's contractions
+        if (!act)
+            continue;
+        if (k + G <= k_end)
+            load_raw(a, c0 + G * kChunk, tid, R);   // in flight during this chunk's contractions
 
         // ---- QK: S[b][r] is cell 16b + 4j + r of this lane's row ----------------
         float S[4][4];
@@ -357,8 +375,41 @@ __global__ __launch_bounds__(kTileThreads) void attn_tile_kernel(AttnArgs a, int
         }
     }
 
+    if constexpr (kFused && G > 1) {
+        // combine the groups: each lane's (M, L, O) has the same row and dims in
+        // every group; groups 1.. publish theirs over their own tiles
+        __syncthreads();
+        // per lane: M, L, two pad words, then O as 8 x 4 floats (16-byte aligned), 144 bytes
+        float *mine = (float *)lds + (w * 64 + lane) * 36;
+        if (gi > 0) {
+            mine[0] = Mrun;
+            mine[1] = Lrun;
+#pragma unroll
+            for (int n = 0; n < 8; ++n)
+                *(floatx4 *)(mine + 4 + 4 * n) = O[n];
+        }
+        __syncthreads();
+        if (gi == 0) {
+            for (int g2 = 1; g2 < G; ++g2) {
+                const float *th = (const float *)(lds_all + g2 * kTileLds) + (w * 64 + lane) * 36;
+                const float M2 = th[0], L2 = th[1];
+                const float M = fmaxf(Mrun, M2);
+                if (M == -INFINITY)
+                    continue;                   // neither has seen a valid cell
+                const float a1 = __builtin_amdgcn_exp2f((Mrun - M) * kLog2e);   // 0 when Mrun = -inf
+                const float a2 = __builtin_amdgcn_exp2f((M2 - M) * kLog2e);
+                Lrun = a1 * Lrun + a2 * L2;
+#pragma unroll
+                for (int n = 0; n < 8; ++n) {
+                    const floatx4 o2 = *(const floatx4 *)(th + 4 + 4 * n);
+                    O[n] = a1 * O[n] + a2 * o2;
+                }
+                Mrun = M;
+            }
+        }
+    }
     if constexpr (kFused) {
-        if (row_ok) {
+        if (row_ok && gi == 0) {
             _Float16 *out = a.out + (int64_t)row * kD + 4 * j;
 #pragma unroll
             for (int n = 0; n < 8; ++n) {
@@ -387,15 +438,16 @@ hipError_t launch_attn_tile(const AttnArgs &a, hipStream_t stream)
 {
     const int64_t n_rb = ((int64_t)a.T * a.H + kTileRows - 1) / kTileRows;
     const int n_parts = (a.C + kSplit - 1) / kSplit;
-    hipLaunchKernelGGL(attn_tile_kernel<false>, dim3((unsigned)(n_rb * n_parts)), dim3(kTileThreads), 0, stream, a,
-                       n_parts);
+    hipLaunchKernelGGL((attn_tile_kernel<false, 1>), dim3((unsigned)(n_rb * n_parts)), dim3(kTileThreads), 0, stream,
+                       a, n_parts);
     return hipGetLastError();
 }
 
 hipError_t launch_attn_merge_tile(const AttnArgs &a, hipStream_t stream)
 {
     const int64_t n_rb = ((int64_t)a.T * a.H + kTileRows - 1) / kTileRows;
-    hipLaunchKernelGGL(attn_tile_kernel<true>, dim3((unsigned)n_rb), dim3(kTileThreads), 0, stream, a, 1);
+    hipLaunchKernelGGL((attn_tile_kernel<true, kFusedGroups>), dim3((unsigned)n_rb), dim3(kTileThreads * kFusedGroups),
+                       0, stream, a, 1);
     return hipGetLastError();
 }
 
