@@ -14,10 +14,11 @@
 // the row's scores become order-preserving 32-bit keys held in registers
 // (thread i holds cells i + 512 j, so every read is coalesced):
 //   * the K-th largest key is found with four 8-bit radix passes from the top
-//     byte down. Each pass histograms the candidates' digit into 256 bins
-//     with one private counter per lane (bin * 64 + lane), so LDS atomics
-//     never collide on an address; the 64 copies are then summed and one wave
-//     scans the bins from the top to pick the digit holding the K-th key;
+//     byte down. The top byte's histogram keeps 32 counters per bin
+//     (bin * 32 + lane % 32), so at most two lanes of a wave add to one
+//     address, and the copies are then summed; the lower bytes count only the keys left in
+//     the chosen bin, into plain 256-bin histograms cleared up front. One wave
+//     scans each histogram from the top to pick the digit holding the K-th key;
 //   * the result is the exact threshold key tau, the count of keys above it
 //     and the number E of keys equal to it that are taken (the first E in
 //     cell order);
@@ -36,10 +37,12 @@ namespace {
 constexpr int kBins = 256;
 
 // LDS layout (the counts of the last phase reuse the histogram)
-constexpr int kLCnt = 0;                               // uint[256 bins][64 lanes]; later uint2[KPT][8 waves]
-constexpr int kLTot = kLCnt + kBins * 64 * 4;          // uint[256] bin totals
-constexpr int kLDec = kLTot + kBins * 4;               // uint[2]: digit, count above it
-constexpr int kSelLds = kLDec + 16;
+constexpr int kCopies = 32;                            // counters per bin in the top byte's histogram
+constexpr int kLCnt = 0;                               // uint[256 bins][32 copies]; later uint2[KPT][waves]
+constexpr int kLTot = kLCnt + kBins * kCopies * 4;     // uint[256] bin totals
+constexpr int kLDec = kLTot + kBins * 4;               // uint[2][2]: digit, count above it (by pass parity)
+constexpr int kLCnt1 = kLDec + 16;                     // uint[3 passes][256]: single-copy histograms
+constexpr int kSelLds = kLCnt1 + 3 * kBins * 4;
 
 // Order-preserving key: larger score, larger key; -0 and +0 share one key.
 __device__ inline uint32_t order_key(float f)
@@ -55,6 +58,7 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a)
 {
     constexpr int kSelThreads = NT;
     constexpr int kSelWaves = NT / 64;
+    static_assert(KPT * kSelWaves * 8 <= kBins * kCopies * 4, "the compaction's counts reuse the histogram");
     __shared__ __align__(16) uint8_t lds[kSelLds];
     uint32_t *cnt = (uint32_t *)(lds + kLCnt);
     uint32_t *tot = (uint32_t *)(lds + kLTot);
@@ -87,41 +91,60 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a)
     }
 
     // ---- the K-th largest key, one byte at a time ---------------------------
+    // The top byte sees every key: its histogram keeps 32 counters per bin so
+    // that at most two lanes of a wave add to one address. After it only the keys of
+    // the chosen bin remain (a small share for any spread of scores), so the
+    // three lower bytes count into plain 256-bin histograms, all cleared up
+    // front: two barriers per pass.
+    uint32_t *cnt1 = (uint32_t *)(lds + kLCnt1);
+    for (int q = tid; q < 3 * kBins; q += kSelThreads)
+        cnt1[q] = 0u;
     uint32_t prefix = 0, mask = 0, k_left = (uint32_t)a.K;
 #pragma unroll 1
-    for (int shift = 24; shift >= 0; shift -= 8) {
+    for (int pass = 0; pass < 4; ++pass) {
+        const int shift = 24 - 8 * pass;
+        const uint32_t *hist;                            // the pass's 256 bin totals
+        if (pass == 0) {
+            for (int q = tid; q < kBins * kCopies / 4; q += kSelThreads)
+                ((uint4 *)cnt)[q] = make_uint4(0u, 0u, 0u, 0u);
+            __syncthreads();
 #pragma unroll
-        for (int q = tid; q < kBins * 64 / 4; q += kSelThreads)
-            ((uint4 *)cnt)[q] = make_uint4(0u, 0u, 0u, 0u);
-        __syncthreads();
+            for (int j = 0; j < KPT; ++j)
+                atomicAdd(&cnt[(key[j] >> 24) * kCopies + (lane & (kCopies - 1))], 1u);
+            __syncthreads();
+            {   // bin totals: NT / 256 threads per bin, each summing a share of the copies
+                constexpr int kParts = NT / kBins;
+                const int bin = tid / kParts, part = tid % kParts;
+                const uint4 *src = (const uint4 *)(cnt + bin * kCopies + part * (kCopies / kParts));
+                uint32_t sum = 0;
 #pragma unroll
-        for (int j = 0; j < KPT; ++j)
-            if ((key[j] & mask) == prefix)
-                atomicAdd(&cnt[((key[j] >> shift) & 255u) * 64 + lane], 1u);
-        __syncthreads();
-        {   // bin totals: NT / 256 threads per bin, each summing a share of the 64 lane copies
-            constexpr int kParts = NT / kBins;
-            const int bin = tid / kParts, part = tid % kParts;
-            const uint4 *src = (const uint4 *)(cnt + bin * 64 + part * (64 / kParts));
-            uint32_t s = 0;
+                for (int i = 0; i < kCopies / 4 / kParts; ++i) {
+                    const uint4 v = src[i];
+                    sum += v.x + v.y + v.z + v.w;
+                }
 #pragma unroll
-            for (int i = 0; i < 16 / kParts; ++i) {
-                const uint4 v = src[i];
-                s += v.x + v.y + v.z + v.w;
+                for (int d = 1; d < kParts; d <<= 1)
+                    sum += __shfl_xor(sum, d, 64);
+                if (part == 0)
+                    tot[bin] = sum;
             }
+            __syncthreads();
+            hist = tot;
+        } else {
+            uint32_t *h = cnt1 + (pass - 1) * kBins;
 #pragma unroll
-            for (int d = 1; d < kParts; d <<= 1)
-                s += __shfl_xor(s, d, 64);
-            if (part == 0)
-                tot[bin] = s;
+            for (int j = 0; j < KPT; ++j)
+                if ((key[j] & mask) == prefix)
+                    atomicAdd(&h[(key[j] >> shift) & 255u], 1u);
+            __syncthreads();
+            hist = h;
         }
-        __syncthreads();
         if (w == 0) {
             // lane l holds bins 4l .. 4l+3; suffix sums from the top bin down
             uint32_t b[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                b[i] = tot[4 * lane + i];
+                b[i] = hist[4 * lane + i];
             const uint32_t mine = b[0] + b[1] + b[2] + b[3];
             uint32_t suf = mine;                         // bins 4l .. 255
 #pragma unroll
@@ -143,16 +166,15 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a)
                     }
                     acc += b[i];
                 }
-                dec[0] = (uint32_t)digit;
-                dec[1] = acc;                            // candidates above the chosen digit
+                dec[2 * (pass & 1)] = (uint32_t)digit;
+                dec[2 * (pass & 1) + 1] = acc;           // candidates above the chosen digit
             }
         }
         __syncthreads();
-        const uint32_t digit = dec[0], acc = dec[1];
+        const uint32_t digit = dec[2 * (pass & 1)], acc = dec[2 * (pass & 1) + 1];
         prefix |= digit << shift;
         mask |= 255u << shift;
         k_left -= acc;
-        __syncthreads();                                 // cnt, tot and dec are rewritten next
     }
     const uint32_t tau = prefix;                         // the K-th largest key
     const uint32_t take_eq = k_left;                     // keys equal to tau that are taken (in cell order);
