@@ -113,8 +113,9 @@ def evenly_spaced_ids(pos0: int, T: int, K: int) -> np.ndarray:
 
     Row t (p = pos0 + t) holds every cell 0..p when p + 1 <= K, otherwise
     floor(j * p / (K - 1)) for j = 0..K-1: ascending, unique (the step p/(K-1)
-    is at least 1), and containing the sink cell 0 and the current cell p.
-    The row is padded with -1 to a whole number of 64-cell chunks.
+    is at least 1), and containing the sink cell 0 and the current cell p
+    (K = 1 holds the current cell alone). The row is padded with -1 to a whole
+    number of 64-cell chunks.
     """
     stride = CHUNK * ((K + CHUNK - 1) // CHUNK)
     ids = np.full((T, stride), -1, dtype=np.int32)
@@ -123,6 +124,8 @@ def evenly_spaced_ids(pos0: int, T: int, K: int) -> np.ndarray:
         p = pos0 + t
         if p + 1 <= K:
             ids[t, : p + 1] = np.arange(p + 1, dtype=np.int32)
+        elif K == 1:
+            ids[t, 0] = p
         else:
             ids[t, :K] = (j * p) // (K - 1)
     return ids
