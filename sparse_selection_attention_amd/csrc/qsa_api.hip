@@ -175,7 +175,7 @@ qsa_status qsa_attn(const void *q, const int8_t *kq, const int8_t *vq,
         return fail(QSA_ERR_ARG, "qsa_attn: NULL part");
     if (!aligned(part, 256))
         return fail(QSA_ERR_ARG, "qsa_attn: misaligned part (256 B)");
-    const int64_t n_blocks = ((int64_t)a.C + qsa::kAttnWaves - 1) / qsa::kAttnWaves * T;   // (chunk group, token)
+    const int64_t n_blocks = (int64_t)a.C * T;   // one wave per (chunk, token)
     const int64_t per_xcd = (n_blocks + 7) / 8;
     if (per_xcd * 8 > INT32_MAX)
         return fail(QSA_ERR_ARG, "qsa_attn: T * chunks too large for one launch");

@@ -8,8 +8,9 @@
 // denominator and a partial output per chunk; each V value read once per cell
 // for all heads).
 //
-// Design on CDNA4. A workgroup owns four consecutive chunks of one query token,
-// one 64-lane wave per chunk:
+// Design on CDNA4. For the chunk records, one 64-lane wave is one workgroup and
+// owns one chunk of one query token; the fused dispatch gives a token one
+// workgroup whose waves sweep its chunks. Per chunk:
 //   * lane c reads slot c's id; a ballot gives the chunk's valid mask;
 //   * the 64 cells' K and V rows are read once for all heads: MFMA tiles put the
 //     heads (up to 16) on one tile dimension and the cells on the other;
@@ -17,8 +18,9 @@
 //     of distinct rows each group of four lanes touches: K rows are copied into
 //     LDS with direct-to-LDS loads of 16 bytes per lane, eight lanes per row,
 //     and read back in MFMA operand order; V rows are read four full rows per
-//     instruction straight into the PV operand registers; the token's q is
-//     copied into LDS once per workgroup and shared by its four waves;
+//     instruction straight into the PV operand registers; a records wave reads
+//     its q operands straight from memory (a token's 3 KB of q stay in L2 for
+//     all its chunks), the fused workgroup copies q into LDS once for its waves;
 //   * the K tile and the q rows are XOR-swizzled in 16-byte granules so that
 //     the operand reads hit distinct LDS banks;
 //   * QK: v_mfma_f32_16x16x32_f16 with A = K rows (16 cells x 32 dims of one
@@ -43,9 +45,9 @@
 //     nearly cancel;
 //   * int8 bytes become fp16 with one SDWA conversion each, the byte picked
 //     straight out of the loaded dword.
-// Workgroups are ordered by chunk group first (all tokens of chunks 0-3, then
-// chunks 4-7, ...) and each XCD walks a contiguous range of them, so the cells
-// one XCD gathers stay within a narrow band of the cache, served from its L2.
+// Record waves are ordered by chunk first (all tokens of chunk 0, then chunk
+// 1, ...) and each XCD walks a contiguous range of them, so the cells one XCD
+// gathers stay within a narrow band of the cache, served from its L2.
 #include "qsa_internal.h"
 #include "qsa_device.h"
 
@@ -54,9 +56,9 @@ namespace {
 
 using namespace dev;
 
-constexpr int kWaves = kAttnWaves;         // chunks (one per wave) per workgroup
+constexpr int kWaves = kAttnWaves;         // waves of a fused workgroup, at most
 
-// LDS layout of one workgroup (dynamic size: the q rows depend on H)
+// LDS layout: one wave region per wave, then (fused workgroup only) the q rows
 constexpr int kKTileBytes = kChunk * kD;                 // 8 KB of K rows per wave
 constexpr int kWaveBytes = kKTileBytes + kChunk * 8      // K tile, K scales (fp16 x 4)
                            + kChunk * 8 + kChunk * 4;    // V scales (group-major), cell ids
@@ -300,39 +302,35 @@ __device__ inline void pv_accumulate(const float (&P)[4][4], const uint2 (&vraw)
 
 // ---- chunk records (qsa_attn) ---------------------------------------------
 
-__global__ __launch_bounds__(64 * kWaves) void attn_kernel(AttnArgs a)
+__global__ __launch_bounds__(64) void attn_kernel(AttnArgs a)
 {
-    extern __shared__ __align__(16) uint8_t lds[];
+    __shared__ __align__(16) uint8_t lds[kWaveBytes];
 
-    const int lane = threadIdx.x & 63;
-    const int w = threadIdx.x >> 6;
+    const int lane = threadIdx.x;
     const int j = lane >> 4;        // 16-lane row of the wave
     const int c16 = lane & 15;      // column inside a 16-wide MFMA tile
 
-    // each XCD (workgroup id mod 8) walks a contiguous range of workgroups
+    // one wave per (chunk, token), chunk-major; each XCD (workgroup id mod 8)
+    // walks a contiguous range of them
     const int lb = (blockIdx.x & 7) * a.blocks_per_xcd + (blockIdx.x >> 3);
     if (lb >= a.n_blocks)
-        return;                     // uniform over the workgroup
-    const int kg = lb / a.T;
-    const int t = lb - kg * a.T;
-    const int k = kWaves * kg + w;
-    const bool has_chunk = k < a.C;
+        return;
+    const int k = lb / a.T;
+    const int t = lb - k * a.T;
+    const WaveLds L = wave_lds(lds, 0);
 
-    const WaveLds L = wave_lds(lds, w);
-    uint8_t *qrows = lds + kWaves * kWaveBytes;
-
-    copy_q_rows(a, qrows, t, w, kWaves, lane);
+    // q operand straight from memory: head c16, dims 32g + 8j .. +7; a padding
+    // head (c16 >= H) repeats head H-1, and its results are never written
+    half8 qop[4];
+    {
+        const _Float16 *qr = a.q + ((int64_t)t * a.H + min(c16, a.H - 1)) * kD + 8 * j;
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+            qop[g] = *(const half8 *)(qr + 32 * g);
+    }
     uint2 ks = make_uint2(0u, 0u), vs = make_uint2(0u, 0u);
     uint2 vraw[2][8];
-    uint64_t mask = 0;
-    if (has_chunk)
-        mask = issue_chunk(a, L, t, k, lane, j, c16, ks, vs, vraw);
-    // direct-to-LDS copies (q, K) complete, then the whole workgroup sees them
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-
-    if (!has_chunk)
-        return;
+    const uint64_t mask = issue_chunk(a, L, t, k, lane, j, c16, ks, vs, vraw);
     const int64_t rec = ((int64_t)t * a.C + k) * a.H;
     if (mask == 0) {                 // empty chunk: (-inf, +0), o left alone
         if (lane < a.H) {
@@ -341,11 +339,11 @@ __global__ __launch_bounds__(64 * kWaves) void attn_kernel(AttnArgs a)
         }
         return;
     }
+    __builtin_amdgcn_s_waitcnt(0);   // the K tile copy has landed
+    wave_sync_lds();
 
     float down;
     const bool renorm = stage_scales(L, lane, ks, vs, down);
-    half8 qop[4];
-    q_operand(a, qrows, j, c16, qop);
     float S[4][4];
     chunk_scores(a.scale, L, qop, mask, j, c16, S);
     const float mx = chunk_max(S);
@@ -506,8 +504,7 @@ __global__ __launch_bounds__(64 * kWaves) void attn_merge_kernel(AttnArgs a)
 
 hipError_t launch_attn(const AttnArgs &a, hipStream_t stream)
 {
-    dim3 grid(8 * a.blocks_per_xcd), block(64 * kWaves);
-    hipLaunchKernelGGL(attn_kernel, grid, block, attn_lds_bytes(kWaves, a.H), stream, a);
+    hipLaunchKernelGGL(attn_kernel, dim3(8 * a.blocks_per_xcd), dim3(64), 0, stream, a);
     return hipGetLastError();
 }
 

@@ -11,7 +11,7 @@ constexpr int kD = 128;       // head dim implemented by this build
 constexpr int kChunk = 64;    // slots per chunk
 constexpr int kGroup = 32;    // dims per fp16 scale
 constexpr int kMaxHeads = 16; // heads fill the 16-wide MFMA tile dimension
-constexpr int kAttnWaves = 4; // consecutive chunks of one token per attention workgroup
+constexpr int kAttnWaves = 4; // waves of a fused attention workgroup (one token)
 constexpr int kMaxCells = 1 << 25; // cache rows addressed with 32-bit byte offsets
 
 struct AttnArgs {
@@ -28,7 +28,7 @@ struct AttnArgs {
     float *m;                 // [T][C][H]
     float *l;                 // [T][C][H]
     _Float16 *out;            // [T][H][D]      merged output (qsa_attn_merge)
-    int32_t n_blocks;         // workgroups that carry work: ceil(C / 4) chunk groups x T tokens
+    int32_t n_blocks;         // workgroups that carry work: C x T one-wave records, T fused
     int32_t blocks_per_xcd;   // workgroups each XCD walks through
 };
 

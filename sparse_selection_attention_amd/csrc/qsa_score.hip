@@ -57,34 +57,35 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a, int n_row_tiles
         float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
         const int t = r0 + row;
         if (t < a.T) {
+            // every head's read is issued before the first add (one round trip
+            // per row, not one per few heads); the adds keep head order
             const float *qr = a.q + (int64_t)t * a.Hs * kD + 4 * c4;
-            int h = 0;
-            for (; h + 4 <= a.Hs; h += 4) {          // four independent loads in flight
-                float4 v[4];
+            // (indexes past Hs re-read the last head, unconditionally, so that no
+            // load is tied to a branch; those values are not added)
+            float4 v[kMaxHeads];
 #pragma unroll
-                for (int u = 0; u < 4; ++u)
-                    v[u] = *(const float4 *)(qr + (int64_t)(h + u) * kD);
+            for (int h = 0; h < kMaxHeads; ++h)
+                v[h] = *(const float4 *)(qr + (int64_t)min(h, a.Hs - 1) * kD);
 #pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    acc.x += v[u].x; acc.y += v[u].y; acc.z += v[u].z; acc.w += v[u].w;
+            for (int h = 0; h < kMaxHeads; ++h)
+                if (h < a.Hs) {
+                    acc.x += v[h].x; acc.y += v[h].y; acc.z += v[h].z; acc.w += v[h].w;
                 }
-            }
-            for (; h < a.Hs; ++h) {
-                const float4 v = *(const float4 *)(qr + (int64_t)h * kD);
-                acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
-            }
         }
         *(float4 *)&sq[row][4 * c4] = acc;
     }
 
     // K tile staging: thread tid moves 8 float4s, rows (tid >> 5) + 8i, column 4 * (tid & 31)
-    float4 kreg[8];
+    floatx4 kreg[8];
     auto fetch = [&](int ct) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            const int c = ct * kTile + (tid >> 5) + 8 * i;
-            kreg[i] = c < a.n_cells ? *(const float4 *)(a.k + (int64_t)c * kD + 4 * (tid & 31))
-                                    : make_float4(0.f, 0.f, 0.f, 0.f);
+            // a cell past the cache stages a copy of the last cell: a K row
+            // feeds only its own score column, and such a column lies past
+            // every row's causal edge (n_cells >= pos0 + T), so its value is
+            // never written; the load stays unconditional, free of any branch
+            const int c = min(ct * kTile + (tid >> 5) + 8 * i, a.n_cells - 1);
+            kreg[i] = *(const floatx4 *)(a.k + (int64_t)c * kD + 4 * (tid & 31));
         }
     };
     fetch(ct0);
@@ -99,7 +100,7 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a, int n_row_tiles
             break;                           // uniform: later tiles are further out
 #pragma unroll
         for (int i = 0; i < 8; ++i)
-            *(float4 *)&sk[(tid >> 5) + 8 * i][4 * (tid & 31)] = kreg[i];
+            *(floatx4 *)&sk[(tid >> 5) + 8 * i][4 * (tid & 31)] = kreg[i];
         __syncthreads();
         if (ct + 1 < ct0 + run_len && (int64_t)(c0 + kTile) <= last_causal)
             fetch(ct + 1);                   // in flight during the contraction
