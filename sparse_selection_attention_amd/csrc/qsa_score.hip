@@ -11,15 +11,38 @@
 // and later cells are not written.
 //
 // Design on CDNA4. The head sum is linear, so sum_h (q_h . k) = (sum_h q_h) . k:
-// a 256-thread workgroup adds the heads of its 64 query rows once into LDS and
-// then walks a run of consecutive 64-cell column tiles, each one a
-// 64 x 64 x 128 fp32 contraction on v_mfma_f32_16x16x4_f32 (each wave a 32 x 32
-// quadrant as four 16 x 16 accumulators). The next K tile is fetched into
-// registers while the current one is multiplied. Tiles wholly beyond the last
-// causal cell of their rows end the walk (such tiles hold no tail either, since
-// the tail never crosses a 64-cell boundary). Workgroups are ordered so that
-// each XCD (workgroup id mod 8) walks a contiguous range of column runs: the K
-// rows one XCD reads stay within its own L2.
+// a 256-thread workgroup adds the heads of its 64 query rows once and then
+// walks a run of consecutive 64-cell column tiles, each one a 64 x 64 x 128
+// contraction; each wave owns a 32 x 32 quadrant as four 16 x 16 accumulators.
+//
+// The contraction runs on the bf16 matrix cores (v_mfma_f32_16x16x32_bf16, 16
+// times the fp32 MFMA rate) with both operands split into two bf16 parts,
+// x = x_hi + x_lo, x_hi = bf16(x) and x_lo = bf16(x - x_hi), contracted as
+// hi*hi + hi*lo + lo*hi with fp32 accumulation. bf16 keeps 8 significant bits,
+// so |x - x_hi| <= 2^-8 |x| and |x - x_hi - x_lo| <= 2^-16 |x|; the dropped
+// lo*lo term is at most 2^-16 |q||k| too, so every product is within
+// 3 * 2^-16 |q||k| and a score within 4.6e-5 * scale * sum_d |q_d||k_d|. bf16
+// has fp32's exponent range, so no scaling is needed; x_hi is taken from x
+// clamped to the largest finite bf16, so an fp32 value beyond it splits into
+// that maximum plus a finite remainder, and an infinity into the maximum plus
+// an infinity, whose products are infinite exactly as in fp32. (A low part
+// below 2^-126 is subnormal in bf16; scores of values that small lose it.)
+//
+// The score scale multiplies the head-summed q once, before its split
+// (scale * (q . k) = (scale * q) . k up to rounding), and each wave keeps its
+// 32 rows' split operands in registers for the whole walk. K tiles are split
+// into bf16 parts as they are staged, into two LDS buffers used in turn: the
+// next tile is read into registers before the current one is multiplied and
+// staged into the other buffer after, so one barrier per tile suffices and
+// the reads are issued ahead of the current tile's score stores (loads and
+// stores share one completion counter, so a read issued after the stores
+// could not be waited for without waiting for them too). Tiles wholly beyond
+// the last causal cell of their rows end the walk (such tiles hold no tail
+// either, since the tail never crosses a 64-cell boundary), and tiles wholly
+// inside every row's causal range are stored without per-cell tests.
+// Workgroups are ordered so that each XCD (workgroup id mod 8) walks a
+// contiguous range of column runs: the K rows one XCD reads stay within its
+// own L2.
 #include "qsa_internal.h"
 
 #include <algorithm>
@@ -28,15 +51,73 @@ namespace qsa {
 namespace {
 
 typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kTile = 64;
-constexpr int kPitch = kD + 4;   // LDS row pitch in floats: rows 16 B apart in bank space
-constexpr int kMaxRun = 32;      // column tiles per workgroup, at most
+constexpr int kQPitch = kD + 4;  // fp32 q staging pitch (floats)
+constexpr int kKPitch = kD + 8;  // bf16 K tile pitch (elements): 272-byte rows, so the
+                                 // 16 rows of one operand read start 4 banks apart
+constexpr int kSlots = 512;      // resident workgroups: 256 CUs x 2 (LDS and VGPRs allow two)
+constexpr int kQBytes = kTile * kQPitch * 4;
+constexpr int kKBytes = 2 * kTile * kKPitch * 2;          // one K tile: hi rows, then lo rows
+static_assert(kQBytes <= kKBytes, "the q staging fits in one K buffer");
+constexpr int kLdsBytes = 2 * kKBytes;                     // two K buffers
+constexpr float kBf16Max = 3.38953139e38f;   // largest finite bf16, 0x7f7f
+
+typedef float float2v __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// x = hi + lo as above, for two values (one packed conversion for each part)
+__device__ inline void split2(float x0, float x1, bf16x2 &hi, bf16x2 &lo)
+{
+    const float2v c = {__builtin_amdgcn_fmed3f(x0, -kBf16Max, kBf16Max),
+                       __builtin_amdgcn_fmed3f(x1, -kBf16Max, kBf16Max)};
+    hi = __builtin_convertvector(c, bf16x2);
+    const float2v r = {x0 - (float)hi[0], x1 - (float)hi[1]};
+    lo = __builtin_convertvector(r, bf16x2);
+}
+
+__device__ inline void split8(const float4 &a, const float4 &b, bf16x8 &hi, bf16x8 &lo)
+{
+    bf16x2 h[4], l[4];
+    split2(a.x, a.y, h[0], l[0]);
+    split2(a.z, a.w, h[1], l[1]);
+    split2(b.x, b.y, h[2], l[2]);
+    split2(b.z, b.w, h[3], l[3]);
+    hi = (bf16x8){h[0][0], h[0][1], h[1][0], h[1][1], h[2][0], h[2][1], h[3][0], h[3][1]};
+    lo = (bf16x8){l[0][0], l[0][1], l[1][0], l[1][1], l[2][0], l[2][1], l[3][0], l[3][1]};
+}
+
+__device__ inline void split4(const floatx4 &a, bf16x4 &hi, bf16x4 &lo)
+{
+    bf16x2 h[2], l[2];
+    split2(a.x, a.y, h[0], l[0]);
+    split2(a.z, a.w, h[1], l[1]);
+    hi = (bf16x4){h[0][0], h[0][1], h[1][0], h[1][1]};
+    lo = (bf16x4){l[0][0], l[0][1], l[1][0], l[1][1]};
+}
+
+// the thread's staged K values (rows (tid >> 5) + 8i, column 4 * (tid & 31))
+// split into bf16 high and low parts, into the K buffer at `buf`
+__device__ inline void stage_k(uint8_t *buf, const floatx4 (&kreg)[8], int tid)
+{
+    __bf16 (*kh)[kKPitch] = (__bf16 (*)[kKPitch])buf;
+    __bf16 (*kl)[kKPitch] = (__bf16 (*)[kKPitch])(buf + kTile * kKPitch * 2);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        bf16x4 h, l;
+        split4(kreg[i], h, l);
+        *(bf16x4 *)&kh[(tid >> 5) + 8 * i][4 * (tid & 31)] = h;
+        *(bf16x4 *)&kl[(tid >> 5) + 8 * i][4 * (tid & 31)] = l;
+    }
+}
 
 __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a, int n_row_tiles, int run_len, int n_runs, int blocks_per_xcd)
 {
-    __shared__ float sq[kTile][kPitch];
-    __shared__ float sk[kTile][kPitch];
+    // two bf16 K buffers (hi rows, then lo rows); the fp32 q staging shares the second
+    __shared__ __align__(16) uint8_t lds[kLdsBytes];
+    float (*sq)[kQPitch] = (float (*)[kQPitch])(lds + kKBytes);
 
     const int lb = (blockIdx.x & 7) * blocks_per_xcd + (blockIdx.x >> 3);
     if (lb >= n_row_tiles * n_runs)
@@ -46,6 +127,8 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a, int n_row_tiles
     const int r0 = rt * kTile;
     const int last_row = min(a.T, r0 + kTile) - 1;
     const int64_t last_causal = (int64_t)a.pos0 + last_row;
+    const int64_t first_causal = (int64_t)a.pos0 + r0;    // the tile's first row's last causal cell
+    const bool full_rows = r0 + kTile <= a.T;
     const int ct0 = run * run_len;
     if ((int64_t)ct0 * kTile > last_causal)
         return;
@@ -94,16 +177,40 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a, int n_row_tiles
     const int j = lane >> 4, c16 = lane & 15;
     const int rq = 32 * (w >> 1), cq = 32 * (w & 1);   // this wave's quadrant
 
-    for (int ct = ct0; ct < ct0 + run_len; ++ct) {
+    // A operands, held for the whole walk: row rq + 16 mi + c16, dims 32 ks + 8j .. +7
+    __syncthreads();
+    bf16x8 ah[2][4], al[2][4];
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            // the score scale goes on q here, once: scale * (q . k) = (scale * q) . k
+            const float *src = &sq[rq + 16 * mi + c16][32 * ks + 8 * j];
+            float4 u = *(const float4 *)src, v = *(const float4 *)(src + 4);
+            u.x *= a.scale; u.y *= a.scale; u.z *= a.scale; u.w *= a.scale;
+            v.x *= a.scale; v.y *= a.scale; v.z *= a.scale; v.w *= a.scale;
+            split8(u, v, ah[mi][ks], al[mi][ks]);
+        }
+    stage_k(lds, kreg, tid);                 // the first tile into buffer 0
+    __syncthreads();                         // buffer 0 complete; the q staging is free
+
+    // Per tile: issue the next tile's reads, multiply this one, then wait for
+    // the reads and stage the next tile into the other buffer before storing
+    // this tile's scores. A wait for reads issued before the previous tile's
+    // stores then finds those stores long finished (loads and stores share
+    // one counter), and one barrier per tile suffices.
+    int b = 0;
+    for (int ct = ct0; ct < ct0 + run_len; ++ct, b ^= 1) {
         const int c0 = ct * kTile;
         if ((int64_t)c0 > last_causal)
             break;                           // uniform: later tiles are further out
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-            *(floatx4 *)&sk[(tid >> 5) + 8 * i][4 * (tid & 31)] = kreg[i];
-        __syncthreads();
-        if (ct + 1 < ct0 + run_len && (int64_t)(c0 + kTile) <= last_causal)
-            fetch(ct + 1);                   // in flight during the contraction
+        // the next tile, or (the walk's last tile) this one again: the reads and
+        // the staging below run on every tile, with no branch around them
+        const bool next = ct + 1 < ct0 + run_len && (int64_t)(c0 + kTile) <= last_causal;
+        fetch(next ? ct + 1 : ct);
+        __builtin_amdgcn_sched_barrier(0);   // the reads go out before the contraction
+        const __bf16 (*kh)[kKPitch] = (const __bf16 (*)[kKPitch])(lds + b * kKBytes);
+        const __bf16 (*kl)[kKPitch] = (const __bf16 (*)[kKPitch])(lds + b * kKBytes + kTile * kKPitch * 2);
 
         floatx4 acc[2][2];
 #pragma unroll
@@ -111,62 +218,72 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a, int n_row_tiles
 #pragma unroll
             for (int ni = 0; ni < 2; ++ni)
                 acc[mi][ni] = (floatx4){0.f, 0.f, 0.f, 0.f};
-        // k-slot j of MFMA (u, e) is dim 4 * (4u + j) + e, for A and B alike
-#pragma unroll 4
-        for (int u = 0; u < 8; ++u) {
-            float4 av[2], bv[2];
 #pragma unroll
-            for (int mi = 0; mi < 2; ++mi)
-                av[mi] = *(const float4 *)&sq[rq + 16 * mi + c16][4 * (4 * u + j)];
+        for (int ks = 0; ks < 4; ++ks) {
+            // B operand: cell cq + 16 ni + c16, dims 32 ks + 8j .. +7
+            bf16x8 bh[2], bl[2];
 #pragma unroll
-            for (int ni = 0; ni < 2; ++ni)
-                bv[ni] = *(const float4 *)&sk[cq + 16 * ni + c16][4 * (4 * u + j)];
+            for (int ni = 0; ni < 2; ++ni) {
+                bh[ni] = *(const bf16x8 *)&kh[cq + 16 * ni + c16][32 * ks + 8 * j];
+                bl[ni] = *(const bf16x8 *)&kl[cq + 16 * ni + c16][32 * ks + 8 * j];
+            }
             // the four accumulators are independent: interleave them between steps
 #pragma unroll
             for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
                 for (int ni = 0; ni < 2; ++ni)
-                    acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[mi].x, bv[ni].x, acc[mi][ni], 0, 0, 0);
+                    acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[mi][ks], bh[ni], acc[mi][ni], 0, 0, 0);
 #pragma unroll
             for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
                 for (int ni = 0; ni < 2; ++ni)
-                    acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[mi].y, bv[ni].y, acc[mi][ni], 0, 0, 0);
+                    acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[mi][ks], bl[ni], acc[mi][ni], 0, 0, 0);
 #pragma unroll
             for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
                 for (int ni = 0; ni < 2; ++ni)
-                    acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[mi].z, bv[ni].z, acc[mi][ni], 0, 0, 0);
-#pragma unroll
-            for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-                for (int ni = 0; ni < 2; ++ni)
-                    acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[mi].w, bv[ni].w, acc[mi][ni], 0, 0, 0);
+                    acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al[mi][ks], bh[ni], acc[mi][ni], 0, 0, 0);
         }
+        // the staging waits for the reads: keep it behind the contraction
+        __builtin_amdgcn_sched_barrier(0);
+        stage_k(lds + (b ^ 1) * kKBytes, kreg, tid);   // unread after the last tile
 
         // D layout: lane (j, c16) holds rows 4j + r, column c16 of each 16 x 16 tile
+        if (full_rows && (int64_t)c0 + kTile - 1 <= first_causal) {
+            // every cell of the tile is causal for every row of the tile
 #pragma unroll
-        for (int mi = 0; mi < 2; ++mi)
+            for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int t = r0 + rq + 16 * mi + 4 * j + r;
-                if (t >= a.T)
-                    continue;
-                const int64_t p = (int64_t)a.pos0 + t;
-                int64_t tail_end = ((p + kTile) / kTile) * kTile;    // 64 * ceil((p + 1) / 64)
-                if (tail_end > a.row_stride)
-                    tail_end = a.row_stride;
-                float *row = a.scores + (int64_t)t * a.row_stride;
+                for (int r = 0; r < 4; ++r) {
+                    float *row = a.scores + (int64_t)(r0 + rq + 16 * mi + 4 * j + r) * a.row_stride + c0 + cq + c16;
 #pragma unroll
-                for (int ni = 0; ni < 2; ++ni) {
-                    const int64_t c = c0 + cq + 16 * ni + c16;
-                    if (c <= p)
-                        row[c] = a.scale * acc[mi][ni][r];
-                    else if (c < tail_end)
-                        row[c] = a.dead;
+                    for (int ni = 0; ni < 2; ++ni)
+                        row[16 * ni] = acc[mi][ni][r];
                 }
-            }
-        __syncthreads();                     // sk is rewritten next
+        } else {
+#pragma unroll
+            for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int t = r0 + rq + 16 * mi + 4 * j + r;
+                    if (t >= a.T)
+                        continue;
+                    const int64_t p = (int64_t)a.pos0 + t;
+                    int64_t tail_end = ((p + kTile) / kTile) * kTile;    // 64 * ceil((p + 1) / 64)
+                    if (tail_end > a.row_stride)
+                        tail_end = a.row_stride;
+                    float *row = a.scores + (int64_t)t * a.row_stride;
+#pragma unroll
+                    for (int ni = 0; ni < 2; ++ni) {
+                        const int64_t c = c0 + cq + 16 * ni + c16;
+                        if (c <= p)
+                            row[c] = acc[mi][ni][r];
+                        else if (c < tail_end)
+                            row[c] = a.dead;
+                    }
+                }
+        }
+        __syncthreads();                     // the next tile is staged; this buffer is free
     }
 }
 
@@ -176,11 +293,13 @@ hipError_t launch_score(const ScoreArgs &a, hipStream_t stream)
 {
     const int64_t cells = (int64_t)a.pos0 + a.T;
     const int n_col_tiles = (int)((cells + kTile - 1) / kTile);
-    // longer runs share the head-summed q over more tiles; shorter runs spread
-    // the short rows of a prompt start over more workgroups
-    const int run_len = std::max(4, std::min(kMaxRun, (n_col_tiles + 15) / 16));
-    const int n_runs = (n_col_tiles + run_len - 1) / run_len;
     const int n_row_tiles = (a.T + kTile - 1) / kTile;
+    // as many column runs per row tile as fill the chip's workgroup slots in
+    // one round, so that few query rows still spread over the chip, but at
+    // least four tiles per run to share each workgroup's head sum and split
+    const int want_runs = std::max(1, std::min(n_col_tiles, kSlots / n_row_tiles));
+    const int run_len = std::max(4, (n_col_tiles + want_runs - 1) / want_runs);
+    const int n_runs = (n_col_tiles + run_len - 1) / run_len;
     const int64_t blocks = (int64_t)n_runs * n_row_tiles;
     const int per_xcd = (int)((blocks + 7) / 8);
     hipLaunchKernelGGL(score_kernel, dim3(8 * per_xcd), dim3(256), 0, stream, a, n_row_tiles, run_len, n_runs, per_xcd);
