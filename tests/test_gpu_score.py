@@ -6,6 +6,7 @@ import pytest
 
 from sparse_selection_attention_amd import synth
 
+import oracle
 from gpu_util import check_score_case, run_score
 
 pytestmark = pytest.mark.gpu
@@ -49,3 +50,65 @@ def test_score_determinism():
     a = run_score(sc)
     b = run_score(sc)
     assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+def _compare_causal(sc, g, rows):
+    """Oracle comparison on whole causal rows, non-finite values included:
+    finite oracle scores within 1e-4 of the error scale, infinities with the
+    same sign, NaN where the oracle has NaN."""
+    A_q = np.abs(sc.q.astype(np.float64)).sum(axis=1)
+    for t in rows:
+        p = sc.pos0 + t
+        r = oracle.score(sc.q[t: t + 1], sc.k, p, sc.scale, sc.dead, sc.row_stride)[0, : p + 1]
+        x = g[t, : p + 1].astype(np.float64)
+        nan = np.isnan(r)
+        assert np.array_equal(np.isnan(x), nan), "row %d: NaN pattern" % t
+        inf = np.isinf(r)
+        assert np.array_equal(x[inf], r[inf]), "row %d: infinities" % t
+        fin = ~(nan | inf)
+        with np.errstate(invalid="ignore", over="ignore"):
+            A = abs(float(sc.scale)) * (np.abs(sc.k[: p + 1].astype(np.float64)) @ A_q[t])
+        err = np.abs(x[fin] - r[fin])
+        assert np.all(np.isfinite(x[fin])), "row %d: a finite oracle score came out non-finite" % t
+        assert np.all(err <= 1e-4 * np.maximum(np.abs(r[fin]), A[fin])), "row %d: err/A %g" % (t, (err / A[fin]).max())
+
+
+def test_scores_beyond_the_bf16_range():
+    """Operands above the largest finite bf16 (3.3895e38, below fp32's 3.4028e38)
+    still give finite scores within the bound: the kernel's high part is taken
+    from the clamped value and the remainder is finite."""
+    T, pos0, Hs = 70, 100, 1
+    sc = synth.score_case(T=T, pos0=pos0, Hs=Hs, scale=1.0)
+    rng = np.random.default_rng(3)
+    n = sc.n_cells
+    sc.q[:, 0, 0] = np.float32(3.40e38) * rng.choice([-1.0, 1.0], T).astype(np.float32)
+    sc.k[:, 0] = (rng.uniform(1e-3, 1e-2, n) * rng.choice([-1.0, 1.0], n)).astype(np.float32)
+    sc.k[:, 1] = np.float32(3.395e38) * rng.choice([-1.0, 1.0], n).astype(np.float32)
+    sc.q[:, 0, 1] = (rng.uniform(1e-4, 1e-3, T)).astype(np.float32)
+    sc.k[:, 2:] = 0.0                                  # keep every score within fp32 range
+    g = run_score(sc)
+    _compare_causal(sc, g, range(T))
+
+
+def test_infinite_and_nan_operands():
+    """An infinite q or K component gives an infinity of the same sign (the
+    other operand's matching component is a normal number), and NaN stays NaN."""
+    T, pos0, Hs = 66, 30, 2
+    sc = synth.score_case(T=T, pos0=pos0, Hs=Hs, scale=0.5)
+    rng = np.random.default_rng(4)
+    n = sc.n_cells
+    sc.k[:, 5] = (rng.uniform(0.5, 1.0, n) * rng.choice([-1.0, 1.0], n)).astype(np.float32)
+    sc.q[3, 1, 5] = np.inf                             # row 3: +inf times K's column 5
+    sc.q[40, 0, 5] = -np.inf                           # row 40: -inf
+    sc.q[50, 0, 7] = np.nan                            # row 50: NaN
+    sc.q[:, :, 9] = np.abs(sc.q[:, :, 9]) + 0.5       # column 9 of q: normal, positive
+    sc.k[17, 9] = np.inf                               # cell 17: +inf for every row ...
+    sc.k[17, 5] = 0.75                                 # ... also row 3's (+inf from both sides)
+    g = run_score(sc)
+    assert np.isinf(g[3, : pos0 + 4]).all() and g[3, 17] == np.inf
+    row40 = g[40, : pos0 + 41]
+    assert np.isnan(row40[17])                         # -inf from column 5 meets +inf from column 9
+    assert np.isinf(np.delete(row40, 17)).all()
+    assert np.isnan(g[50, : pos0 + 51]).all()
+    assert (g[[0, 20, 65], 17] == np.inf).all()
+    _compare_causal(sc, g, [0, 3, 17, 20, 40, 50, 65])
