@@ -117,7 +117,7 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print("bench.py: this build runs on one GPU; --gpus %d is not supported (the path would shard by "
+        print("bench.py: the benchmark runs on one GPU; --gpus %d is not supported (the path would shard by "
               "query token, with no exchange between GPUs)" % args.gpus, file=sys.stderr)
         return 2
     if int(os.environ.get("WORLD_SIZE", "1")) > 1:

@@ -14,7 +14,7 @@
  *   QSA_OK              success (also for T == 0, which enqueues nothing)
  *   QSA_ERR_ARG         a required pointer is NULL or misaligned, or a size is
  *                       negative or inconsistent; nothing was enqueued
- *   QSA_ERR_UNSUPPORTED a shape this build does not implement (D != 128, more
+ *   QSA_ERR_UNSUPPORTED a shape the library does not implement (D != 128, more
  *                       than 16 heads, more than 2^25 cached rows) or a device
  *                       that is not gfx950
  *   QSA_ERR_DEVICE      a HIP runtime call failed (message in qsa_last_error)
@@ -81,7 +81,7 @@ typedef enum {
  *          (else poison), with C = ceil((pos0 + T) / 64); ids_stride is ignored.
  * pos0     cache position of token 0 (>= 0); T query tokens (>= 0)
  * H        query heads sharing the one K/V head, 1..16
- * D        head dim; this build implements D == 128 only
+ * D        head dim; the library implements D == 128 only
  * scale    softmax scale applied to every dot product
  * part     qsa_part_bytes(T, H, D, C) bytes, 256-byte aligned; laid out as
  *          o[T][C][H][D] fp32, then m[T][C][H] fp32, then l[T][C][H] fp32,
@@ -147,7 +147,7 @@ QSA_API qsa_status qsa_merge(const void *part, int32_t n_chunks, int32_t T, int3
  * q        fp32 [T][Hs][D], 16-byte aligned;  Hs in 1..16
  * k        fp32 [n_cells][D], 16-byte aligned; n_cells >= pos0 + T
  * scores   fp32 [T][row_stride]; row_stride >= pos0 + T; 4-byte aligned
- * D        this build implements D == 128 only
+ * D        the library implements D == 128 only
  */
 QSA_API qsa_status qsa_score(const float *q, const float *k, int32_t n_cells, int32_t pos0,
                      int32_t T, int32_t Hs, int32_t D, float scale, float dead,
@@ -174,7 +174,7 @@ QSA_API qsa_status qsa_score(const float *q, const float *k, int32_t n_cells, in
  * kq, vq        int8 [n_cells_cap][D], 8-byte aligned
  * ksc, vsc      fp16 [n_cells_cap][D/32], 8-byte aligned
  * cell0         first cell written; cell0 + n_rows <= n_cells_cap
- * D             this build implements D == 128 only
+ * D             the library implements D == 128 only
  * n_rows == 0 is a no-op. Bad arguments return QSA_ERR_ARG / QSA_ERR_UNSUPPORTED
  * before anything is enqueued.
  */

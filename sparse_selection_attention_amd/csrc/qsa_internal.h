@@ -7,7 +7,7 @@
 
 namespace qsa {
 
-constexpr int kD = 128;       // head dim implemented by this build
+constexpr int kD = 128;       // the one head dim the kernels implement
 constexpr int kChunk = 64;    // slots per chunk
 constexpr int kGroup = 32;    // dims per fp16 scale
 constexpr int kMaxHeads = 16; // heads fill the 16-wide MFMA tile dimension
