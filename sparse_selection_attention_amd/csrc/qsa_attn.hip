@@ -117,16 +117,19 @@ __device__ inline void q_operand(const AttnArgs &a, const uint8_t *qrows, int j,
 // Chunk k of token t: read the ids, publish them, and issue every gather of the
 // chunk (K rows into the wave's LDS tile, V rows and scales into registers).
 // Returns the ballot of valid slots; nothing is issued for an empty chunk.
-__device__ inline uint64_t issue_chunk(const AttnArgs &a, const WaveLds &L, int t, int k, int lane, int j, int c16,
+// Slot `lane` of chunk k of token t: its cell id, -1 or out of range for an
+// empty slot.
+__device__ inline int32_t slot_id(const AttnArgs &a, int t, int k, int lane)
+{
+    const int64_t slot = (int64_t)k * kChunk + lane;
+    if (a.ids)
+        return a.ids[(int64_t)t * a.ids_stride + slot];
+    return slot <= (int64_t)a.pos0 + t ? (int32_t)slot : -1;
+}
+
+__device__ inline uint64_t issue_chunk(const AttnArgs &a, const WaveLds &L, int32_t id, int lane, int j, int c16,
                                        uint2 &ks, uint2 &vs, uint2 (&vraw)[2][8])
 {
-    const int p = a.pos0 + t;
-    const int64_t slot = (int64_t)k * kChunk + lane;
-    int32_t id;
-    if (a.ids)
-        id = a.ids[(int64_t)t * a.ids_stride + slot];
-    else
-        id = slot <= p ? (int32_t)slot : -1;
     const bool valid = (uint32_t)id < (uint32_t)a.n_cells;
     const int32_t sid = valid ? id : 0;
     const uint64_t mask = __ballot(valid);
@@ -330,7 +333,7 @@ __global__ __launch_bounds__(64) void attn_kernel(AttnArgs a)
     }
     uint2 ks = make_uint2(0u, 0u), vs = make_uint2(0u, 0u);
     uint2 vraw[2][8];
-    const uint64_t mask = issue_chunk(a, L, t, k, lane, j, c16, ks, vs, vraw);
+    const uint64_t mask = issue_chunk(a, L, slot_id(a, t, k, lane), lane, j, c16, ks, vs, vraw);
     const int64_t rec = ((int64_t)t * a.C + k) * a.H;
     if (mask == 0) {                 // empty chunk: (-inf, +0), o left alone
         if (lane < a.H) {
@@ -410,6 +413,9 @@ __global__ __launch_bounds__(64 * kWaves) void attn_merge_kernel(AttnArgs a)
     for (int tt = 0; tt < 8; ++tt)
         O[tt] = (floatx4){0.f, 0.f, 0.f, 0.f};
 
+    // each chunk's slot ids are read one chunk ahead (the last chunk re-reads
+    // its own), so a chunk's gathers start without a round trip for its ids
+    int32_t id_next = slot_id(a, t, min(w, a.C - 1), lane0);
     for (int k = w; k < a.C; k += nw) {
         // lane-derived offsets are rebuilt every chunk (cheap VALU) rather than
         // hoisted out of the loop, where they would pin registers throughout
@@ -418,9 +424,10 @@ __global__ __launch_bounds__(64 * kWaves) void attn_merge_kernel(AttnArgs a)
         const int j = lane >> 4, c16 = lane & 15;
         uint2 ks, vs;
         uint2 vraw[2][8];
-        const uint64_t mask = issue_chunk(a, L, t, k, lane, j, c16, ks, vs, vraw);
+        const uint64_t mask = issue_chunk(a, L, id_next, lane, j, c16, ks, vs, vraw);
         __builtin_amdgcn_s_waitcnt(0);           // the K tile copy has landed
         wave_sync_lds();
+        id_next = slot_id(a, t, min(k + nw, a.C - 1), lane);   // in flight during this chunk
         if (mask == 0)
             continue;                            // uniform: an empty chunk adds nothing
         float down;
