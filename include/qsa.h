@@ -144,6 +144,11 @@ QSA_API qsa_status qsa_merge(const void *part, int32_t n_chunks, int32_t T, int3
  *   scores[t][c] = dead       for p < c < min(64 * ceil((p + 1) / 64), row_stride)
  * and every later cell of the row is left untouched.
  *
+ * Precision: each product is formed on the bf16 matrix cores from operands
+ * split into two bf16 parts, so a score is within 4.6e-5 * |scale| *
+ * sum_d |sum_h q[t][h][d]| * |k[c][d]| of the exact value; infinite operands
+ * give infinite scores as in fp32, and operand parts below 2^-126 are lost.
+ *
  * q        fp32 [T][Hs][D], 16-byte aligned;  Hs in 1..16
  * k        fp32 [n_cells][D], 16-byte aligned; n_cells >= pos0 + T
  * scores   fp32 [T][row_stride]; row_stride >= pos0 + T; 4-byte aligned
@@ -197,7 +202,7 @@ QSA_API qsa_status qsa_quant_append(const float *k, const float *v, int32_t n_ro
  * scores      fp32 [T][row_stride] (e.g. qsa_score's output); row_stride >= pos0 + T
  * ids         int32 [T][ids_stride]; ids_stride a multiple of 64 holding
  *             min(K, pos0 + T) ids, so the rows feed qsa_attn directly
- * This build supports pos0 + T <= 32768 (QSA_ERR_UNSUPPORTED beyond).
+ * The library supports pos0 + T <= 32768 (QSA_ERR_UNSUPPORTED beyond).
  */
 QSA_API qsa_status qsa_select(const float *scores, int64_t row_stride, int32_t pos0, int32_t T, int32_t K,
                       int32_t *ids, int32_t ids_stride, void *stream);
