@@ -13,7 +13,7 @@ import sparse_selection_attention_amd as qsa
 from sparse_selection_attention_amd import synth
 
 from gpu_util import (check_attn_case, check_out, check_records, chunk_magnitude, dev, oracle_token,
-                      oracle_tokens, run_attn, to_dev)
+                      oracle_tokens, run_attn, run_fused, to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -256,6 +256,34 @@ def test_edge_shapes_implicit_rows(T, H, n_cells, pos0):
         r = oracle_token(L, None, pos0, synth.SCALE_1_SQRT_128, t)
         check_out(out[t], r["out64"], "edge t=%d" % t)
         check_records(o[t], m[t], l[t], r, chunk_magnitude(L, None, pos0, synth.SCALE_1_SQRT_128, t, C), t, "edge")
+
+
+@pytest.mark.parametrize("T,H,n_cells,pos0,width", [(3, 1, 100, 90, 70), (9, 5, 300, 250, 128), (40, 16, 700, 600, 321),
+                                                   (2, 16, 64, 62, 1), (6, 3, 520, 500, 450)])
+def test_edge_shapes_explicit_ids(T, H, n_cells, pos0, width):
+    """Explicit ids at head counts 1 .. 16 (so 15 .. 0 padding heads on the MFMA
+    tile), ragged widths, and about a tenth of the slots poisoned with -1, a
+    negative id or an id at or past n_cells: records, two-kernel output and
+    fused output against the oracle on every token."""
+    rng = np.random.default_rng(T + 17 * H)
+    stride = 64 * ((width + 63) // 64)
+    ids = np.full((T, stride), -1, np.int32)
+    for t in range(T):
+        p = pos0 + t
+        k = min(width, p + 1)
+        ids[t, :k] = np.sort(rng.choice(p + 1, k, replace=False))
+        bad = rng.random(stride) < 0.1
+        ids[t, bad] = rng.choice(np.array([-1, -7, n_cells, n_cells + 5], np.int32), int(bad.sum()))
+    L = synth.make_layer(T + H + 1, 0, T, H, n_cells)
+    scale = synth.SCALE_1_SQRT_128
+    print("explicit edge T=%d H=%d n_cells=%d pos0=%d width=%d" % (T, H, n_cells, pos0, width), flush=True)
+    out, o, m, l, C = run_attn(L, ids, pos0, scale)
+    fout = run_fused(L, ids, pos0, scale)
+    for t in range(T):
+        r = oracle_token(L, ids, pos0, scale, t)
+        check_out(out[t], r["out64"], "explicit edge t=%d" % t)
+        check_records(o[t], m[t], l[t], r, chunk_magnitude(L, ids, pos0, scale, t, C), t, "explicit edge")
+        check_out(fout[t], r["out64"], "explicit edge fused t=%d" % t)
 
 
 def test_large_and_tiny_scales():
