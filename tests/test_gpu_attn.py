@@ -286,6 +286,58 @@ def test_edge_shapes_explicit_ids(T, H, n_cells, pos0, width):
         check_out(fout[t], r["out64"], "explicit edge fused t=%d" % t)
 
 
+def test_largest_cache_rows():
+    """A cache of 2^25 rows, the most the library takes: ids reaching its last row
+    exercise the 32-bit byte offsets of the gathers (id * 128 < 2^32). Only the
+    selected rows hold data (8.6 GB of zeros otherwise); the oracle runs on a
+    compact copy of those rows with the ids renumbered."""
+    n_cells = 1 << 25
+    T, H, width = 4, 12, 130
+    pos0 = n_cells - T
+    rng = np.random.default_rng(25)
+    pool = np.unique(np.concatenate([np.arange(n_cells - 70, n_cells),                 # the last rows
+                                     np.arange((1 << 24) - 8, (1 << 24) + 8),          # around 2^24
+                                     rng.choice(pos0, 200, replace=False)]))           # anywhere below
+    compact = synth.make_layer(26, 0, T, H, len(pool))
+    stride = 64 * ((width + 63) // 64)
+    ids = np.full((T, stride), -1, np.int32)
+    ids_c = np.full((T, stride), -1, np.int32)
+    for t in range(T):
+        causal = np.nonzero(pool <= pos0 + t)[0]
+        pick = np.sort(np.concatenate([causal[-20:], rng.choice(causal[:-20], width - 20, replace=False)]))
+        ids[t, :width] = pool[pick]
+        ids_c[t, :width] = pick
+    assert ids.max() == n_cells - T + (T - 1)          # the cache's last row is selected
+    d = dev()
+    idx = torch.from_numpy(pool.astype(np.int64)).to(d)
+    big = {}
+    for name, arr, dt in (("kq", compact.kq, torch.int8), ("vq", compact.vq, torch.int8),
+                          ("ksc", compact.ksc, torch.float16), ("vsc", compact.vsc, torch.float16)):
+        full = torch.zeros((n_cells,) + arr.shape[1:], dtype=dt, device=d)
+        full[idx] = torch.from_numpy(arr).to(d)
+        big[name] = full
+    q = torch.from_numpy(compact.q).to(d)
+    ids_t = torch.from_numpy(ids).to(d)
+    scale = synth.SCALE_1_SQRT_128
+    print("largest cache: n_cells=%d pos0=%d, %d pooled rows" % (n_cells, pos0, len(pool)), flush=True)
+    C = qsa.chunk_count(ids_t, pos0, T)
+    part = qsa.alloc_part(T, H, 128, C)
+    qsa.qsa_attn(q, big["kq"], big["vq"], big["ksc"], big["vsc"], ids_t, pos0, float(scale), part)
+    out = torch.empty((T, H, 128), dtype=torch.float16, device=d)
+    qsa.qsa_merge(part, C, out)
+    fout = torch.empty_like(out)
+    qsa.qsa_attn_merge(q, big["kq"], big["vq"], big["ksc"], big["vsc"], ids_t, pos0, float(scale), fout)
+    torch.cuda.synchronize()
+    o, m, l = [x.cpu().numpy() for x in qsa.part_views(part, T, H, 128, C)]
+    out, fout = out.cpu().numpy(), fout.cpu().numpy()
+    del big, part
+    for t in range(T):
+        r = oracle_token(compact, ids_c, pos0, scale, t)
+        check_out(out[t], r["out64"], "largest cache t=%d" % t)
+        check_records(o[t], m[t], l[t], r, chunk_magnitude(compact, ids_c, pos0, scale, t, C), t, "largest cache")
+        check_out(fout[t], r["out64"], "largest cache fused t=%d" % t)
+
+
 def test_large_and_tiny_scales():
     """V scales far from the configs' range, and large logits: no overflow, parity holds."""
     L, ids, pos0 = probe_case(T=40, seed=7)
