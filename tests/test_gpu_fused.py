@@ -83,8 +83,9 @@ def test_fused_one_cell_selection_is_bitwise():
     assert np.array_equal(out.view(np.uint16), np.repeat(v.astype(np.float16)[:, None, :], H, axis=1).view(np.uint16))
 
 
-def test_fused_poison_and_unselected_data_do_not_matter():
-    L, ids, pos0 = probe_case(seed=12)
+@pytest.mark.parametrize("T", [150, 40])          # a prompt-sized and a decode-sized token count
+def test_fused_poison_and_unselected_data_do_not_matter(T):
+    L, ids, pos0 = probe_case(T=T, seed=12)
     n_cells = L.kq.shape[0]
     a = run_fused(L, ids, pos0, synth.SCALE_1_SQRT_128)
     used = np.zeros(n_cells, bool)
@@ -100,8 +101,9 @@ def test_fused_poison_and_unselected_data_do_not_matter():
     assert np.array_equal(a.view(np.uint16), b.view(np.uint16))
 
 
-def test_fused_determinism():
-    L, ids, pos0 = probe_case(seed=13)
+@pytest.mark.parametrize("T", [150, 40])
+def test_fused_determinism(T):
+    L, ids, pos0 = probe_case(T=T, seed=13)
     a = run_fused(L, ids, pos0, synth.SCALE_1_SQRT_128)
     b = run_fused(L, ids, pos0, synth.SCALE_1_SQRT_128)
     assert np.array_equal(a.view(np.uint16), b.view(np.uint16))
