@@ -53,19 +53,28 @@ def merge_bytes(T, H, D, C, c):
     return int((H * 8 * C + H * 4 * D * c + 2 * H * D).sum()) if hasattr(c, "sum") else None
 
 
-def src_hash(path):
-    return hashlib.sha256(open(path, "rb").read()).hexdigest()
+def src_hash(*paths):
+    """sha256 over the concatenated sources a kernel is built from."""
+    h = hashlib.sha256()
+    for path in paths:
+        h.update(open(path, "rb").read())
+    return h.hexdigest()
 
 
-def read_traffic(profile_md, kernel_src):
+def attn_sources():
+    csrc = os.path.join(ROOT, "sparse_selection_attention_amd", "csrc")
+    return [os.path.join(csrc, f) for f in ("qsa_attn.hip", "qsa_device.h", "qsa_internal.h")]
+
+
+def read_traffic(profile_md, kernel_srcs):
     """HBM bytes per launch from a committed counter summary, if it matches the source."""
     try:
         text = open(profile_md).read()
     except OSError:
         return None
-    m_hash = re.search(r"kernel source sha256:\s*([0-9a-f]{64})", text)
+    m_hash = re.search(r"kernel source sha256[^:]*:\s*([0-9a-f]{64})", text)
     m_bytes = re.search(r"hbm bytes per launch:\s*([0-9]+)", text)
-    if not m_hash or not m_bytes or m_hash.group(1) != src_hash(kernel_src):
+    if not m_hash or not m_bytes or m_hash.group(1) != src_hash(*kernel_srcs):
         return None
     return int(m_bytes.group(1))
 
@@ -181,7 +190,7 @@ def main():
     attn_gbs = a_bytes / attn_avg_s / 1e9
     step_bytes = args.layers * (a_bytes + m_bytes)
     traffic = read_traffic(os.path.join(ROOT, "profiles", "qsa_kernels_hbm_counters_bench_workloads.md"),
-                           os.path.join(ROOT, "sparse_selection_attention_amd", "csrc", "qsa_attn.hip"))
+                           attn_sources())
 
     result = {
         "metric": "query-token*heads/sec + achieved HBM GB/s, T=1984 pos0=30000 attention",

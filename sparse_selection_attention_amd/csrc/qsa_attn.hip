@@ -43,8 +43,8 @@
 //     a single fp16 rounding of p and of v would cost up to 2^-12 |v| per
 //     term, which is too coarse when a chunk holds a few cells whose values
 //     nearly cancel;
-//   * int8 bytes become fp16 with one SDWA conversion each, the byte picked
-//     straight out of the loaded dword.
+//   * int8 bytes become fp16 exactly through a byte permute under a 1024.0
+//     exponent and one packed subtraction, all visible to the compiler.
 // Record waves are ordered by chunk first (all tokens of chunk 0, then chunk
 // 1, ...) and each XCD walks a contiguous range of them, so the cells one XCD
 // gathers stay within a narrow band of the cache, served from its L2.
