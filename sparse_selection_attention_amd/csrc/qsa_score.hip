@@ -39,7 +39,10 @@
 // could not be waited for without waiting for them too). Tiles wholly beyond
 // the last causal cell of their rows end the walk (such tiles hold no tail
 // either, since the tail never crosses a 64-cell boundary), and tiles wholly
-// inside every row's causal range are stored without per-cell tests.
+// inside every row's causal range are stored without per-cell tests. Scores
+// are written with nontemporal stores: a row of scores is written once and
+// read by a later kernel, so it streams past the caches instead of evicting
+// the K rows that the other workgroups are still reading.
 // Workgroups are ordered so that each XCD (workgroup id mod 8) walks a
 // contiguous range of column runs: the K rows one XCD reads stay within its
 // own L2.
@@ -258,7 +261,7 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a, int n_row_tiles
                     float *row = a.scores + (int64_t)(r0 + rq + 16 * mi + 4 * j + r) * a.row_stride + c0 + cq + c16;
 #pragma unroll
                     for (int ni = 0; ni < 2; ++ni)
-                        row[16 * ni] = acc[mi][ni][r];
+                        __builtin_nontemporal_store(acc[mi][ni][r], &row[16 * ni]);
                 }
         } else {
 #pragma unroll
@@ -277,9 +280,9 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a, int n_row_tiles
                     for (int ni = 0; ni < 2; ++ni) {
                         const int64_t c = c0 + cq + 16 * ni + c16;
                         if (c <= p)
-                            row[c] = acc[mi][ni][r];
+                            __builtin_nontemporal_store(acc[mi][ni][r], &row[c]);
                         else if (c < tail_end)
-                            row[c] = a.dead;
+                            __builtin_nontemporal_store(a.dead, &row[c]);
                     }
                 }
         }
