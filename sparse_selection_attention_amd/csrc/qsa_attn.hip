@@ -56,7 +56,8 @@ namespace {
 
 using namespace dev;
 
-constexpr int kWaves = kAttnWaves;         // waves of a fused workgroup, at most
+constexpr int kWaves = kAttnWaves;         // waves of a fused workgroup over many chunks
+constexpr int kWavesMax = 8;               // waves of a fused workgroup over few chunks: one each
 
 // LDS layout: one wave region per wave, then (fused workgroup only) the q rows
 constexpr int kKTileBytes = kChunk * kD;                 // 8 KB of K rows per wave
@@ -381,15 +382,16 @@ __global__ __launch_bounds__(64) void attn_kernel(AttnArgs a)
 
 // ---- attention with the merge in the same dispatch (qsa_attn_merge) --------
 //
-// One workgroup per token, nw = min(C, 4) waves; wave w takes chunks w, w + nw,
-// ... so every workgroup sweeps the chunks in the same order. A wave keeps a
+// One workgroup per token, nw = C waves for up to 8 chunks, else 4; wave w
+// takes chunks w, w + nw, ... so every workgroup sweeps the chunks in the
+// same order. A wave keeps a
 // running max M, denominator L and output O per head: a chunk with max m moves
 // M to max(M, m), its probabilities are taken against the new M and the old
 // (L, O) are rescaled by exp(M_old - M_new) -- the combination of chunk records
 // relative to the largest maximum, accumulated as it goes. The waves' (M, L, O)
 // are then combined the same way through LDS and divided once.
 
-__global__ __launch_bounds__(64 * kWaves) void attn_merge_kernel(AttnArgs a)
+__global__ __launch_bounds__(64 * kWavesMax) void attn_merge_kernel(AttnArgs a)
 {
     extern __shared__ __align__(16) uint8_t lds[];
 
@@ -517,7 +519,9 @@ hipError_t launch_attn(const AttnArgs &a, hipStream_t stream)
 
 hipError_t launch_attn_merge(const AttnArgs &a, hipStream_t stream)
 {
-    const int nw = a.C < kWaves ? a.C : kWaves;
+    // a row of up to kWavesMax chunks (a decode window) gets one wave per
+    // chunk, so that its gathers all go out at once; longer rows take kWaves
+    const int nw = a.C <= kWavesMax ? a.C : kWaves;
     dim3 grid(8 * a.blocks_per_xcd), block(64 * nw);
     hipLaunchKernelGGL(attn_merge_kernel, grid, block, attn_lds_bytes(nw, a.H), stream, a);
     return hipGetLastError();
