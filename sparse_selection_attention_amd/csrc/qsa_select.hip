@@ -22,11 +22,11 @@
 //   * the result is the exact threshold key tau, the count of keys above it
 //     and the number E of keys equal to it that are taken (the first E in
 //     cell order);
-//   * ids are then written in cell order: each wave records, for every block
-//     j of 512 consecutive cells, how many of its 64 cells lie above tau and
-//     how many equal it (ballots); one wave scans those counts in (block,
-//     wave) order, and every thread places its cells from the scanned offsets
-//     plus its lane prefix -- two barriers for the whole row.
+//   * ids are then written in cell order: ballots turn the strided keys into
+//     bit masks of the cells above tau and equal to it, stored in LDS in cell
+//     order; each thread then takes 32 consecutive cells of the masks, one
+//     scan over the threads gives the counts before them, and every thread
+//     writes its selected cells from there -- two barriers for the whole row.
 // Cells past the row (c > p) hold key 0, below every score that is not NaN.
 // Rows of up to 32768 cells (32 keys per thread).
 #include "qsa_internal.h"
@@ -58,7 +58,8 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a)
 {
     constexpr int kSelThreads = NT;
     constexpr int kSelWaves = NT / 64;
-    static_assert(KPT * kSelWaves * 8 <= kBins * kCopies * 4, "the compaction's counts reuse the histogram");
+    static_assert(KPT * kSelWaves * 16 <= kBins * kCopies * 4, "the compaction's masks reuse the histogram");
+    static_assert(kSelWaves <= kBins && KPT <= 32, "wave totals reuse the bin totals; one mask bit per key");
     __shared__ __align__(16) uint8_t lds[kSelLds];
     uint32_t *cnt = (uint32_t *)(lds + kLCnt);
     uint32_t *tot = (uint32_t *)(lds + kLTot);
@@ -181,68 +182,67 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a)
                                                          // the other K - take_eq keys lie above tau
 
     // ---- ids in cell order ----------------------------------------------------
-    // counts of each (block j, wave) pair: block j is cells NT j .. NT j + NT - 1,
-    // wave w holds NT j + 64 w .. +63 of them
-    uint2 *pc = (uint2 *)cnt;                            // [KPT][8 waves]
+    // A ballot turns the keys of block j (cells NT j .. NT j + NT - 1) held by
+    // wave w into the 64-bit masks of cells NT j + 64 w .. +63 above tau and
+    // equal to it: mask word (j, w) covers cells 64 (kSelWaves j + w) .. +63,
+    // so the words in (j, w) order are the row's masks in cell order. Lane j of
+    // each wave gathers block j's words, and one LDS write per wave
+    // stores them.
+    uint4 *words = (uint4 *)cnt;                         // [KPT * kSelWaves] {gt lo, gt hi, eq lo, eq hi}
+    {
+        uint32_t glo = 0, ghi = 0, elo = 0, ehi = 0;
 #pragma unroll
-    for (int j = 0; j < KPT; ++j) {
-        const uint64_t bg = __ballot(key[j] > tau), be = __ballot(key[j] == tau);
-        if (lane == 0)
-            pc[j * kSelWaves + w] = make_uint2((uint32_t)__popcll(bg), (uint32_t)__popcll(be));
+        for (int j = 0; j < KPT; ++j) {
+            const uint64_t bg = __ballot(key[j] > tau), be = __ballot(key[j] == tau);
+            const bool mine = lane == j;
+            glo = mine ? (uint32_t)bg : glo;
+            ghi = mine ? (uint32_t)(bg >> 32) : ghi;
+            elo = mine ? (uint32_t)be : elo;
+            ehi = mine ? (uint32_t)(be >> 32) : ehi;
+        }
+        if (lane < KPT)
+            words[lane * kSelWaves + w] = make_uint4(glo, ghi, elo, ehi);
     }
     __syncthreads();
-    if (w == 0) {
-        // exclusive scan of the KPT * 8 pairs in (block, wave) order; lane l owns
-        // a run of consecutive entries
-        constexpr int kEnt = KPT * kSelWaves;
-        constexpr int kPer = (kEnt + 63) / 64;
-        uint32_t sg = 0, se = 0;
-#pragma unroll
-        for (int i = 0; i < kPer; ++i) {
-            const int e = lane * kPer + i;
-            if (e < kEnt) {
-                const uint2 v = pc[e];
-                sg += v.x;
-                se += v.y;
-            }
-        }
-        uint32_t ig = sg, ie = se;                       // inclusive over lanes
-#pragma unroll
-        for (int d = 1; d < 64; d <<= 1) {
-            const uint32_t og = __shfl_up(ig, d, 64), oe = __shfl_up(ie, d, 64);
-            if (lane >= d) {
-                ig += og;
-                ie += oe;
-            }
-        }
-        uint32_t rg = ig - sg, re = ie - se;             // before this lane's run
-#pragma unroll
-        for (int i = 0; i < kPer; ++i) {
-            const int e = lane * kPer + i;
-            if (e < kEnt) {
-                const uint2 v = pc[e];
-                pc[e] = make_uint2(rg, re);
-                rg += v.x;
-                re += v.y;
-            }
-        }
+    // Thread i now takes cells 32 i .. 32 i + 31, half of word i / 2: the counts
+    // above and equal to tau before its cells come from one scan over the
+    // threads, and its cells are written in order from there.
+    constexpr int kCellThreads = KPT * kSelThreads / 32;
+    uint32_t gt32 = 0, eq32 = 0;
+    if (tid < kCellThreads) {
+        const uint4 wd = words[tid >> 1];
+        gt32 = (tid & 1) ? wd.y : wd.x;
+        eq32 = (tid & 1) ? wd.w : wd.z;
     }
-    __syncthreads();
-    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    // recompute the ballots rather than keep the first loop's (2 x KPT masks
-    // would not fit in scalar registers): tau is hidden from the compiler here
-    uint32_t tau2 = tau;
-    int tid2 = tid;                 // cell indices are rebuilt here, not kept from the reads
-    asm volatile("" : "+v"(tau2), "+v"(tid2));
+    // counts packed as (above << 16) | equal: each is at most 32768 over the row
+    const uint32_t own = ((uint32_t)__popc(gt32) << 16) | (uint32_t)__popc(eq32);
+    uint32_t inc = own;
 #pragma unroll
-    for (int j = 0; j < KPT; ++j) {
-        const bool gt = key[j] > tau2, eq = key[j] == tau2;
-        const uint64_t bg = __ballot(gt), be = __ballot(eq);
-        const uint2 base = pc[j * kSelWaves + w];
-        const uint32_t gt_before = base.x + (uint32_t)__popcll(bg & below);
-        const uint32_t eq_before = base.y + (uint32_t)__popcll(be & below);
-        if (gt || (eq && eq_before < take_eq))
-            ids[gt_before + min(eq_before, take_eq)] = tid2 + kSelThreads * j;
+    for (int d = 1; d < 64; d <<= 1) {
+        const uint32_t o = __shfl_up(inc, d, 64);
+        if (lane >= d)
+            inc += o;
+    }
+    uint32_t *wsum = tot;                                // [kSelWaves] wave totals
+    if (lane == 63)
+        wsum[w] = inc;
+    __syncthreads();
+    uint32_t before = inc - own;
+    for (int v = 0; v < w; ++v)
+        before += wsum[v];
+    const uint32_t gt_before = before >> 16, eq_before = before & 0xffffu;
+    // the first take_eq cells equal to tau are taken: this thread keeps the
+    // lowest of its equal cells while the count before it is short of take_eq
+    uint32_t keep = 0, m = eq32;
+    for (uint32_t k = eq_before; k < take_eq && m != 0; ++k) {
+        keep |= m & (0u - m);
+        m &= m - 1;
+    }
+    uint32_t sel = gt32 | keep;
+    uint32_t slot = gt_before + min(eq_before, take_eq);
+    while (sel != 0) {
+        ids[slot++] = 32 * tid + __builtin_ctz(sel);
+        sel &= sel - 1;
     }
     for (int q = a.K + tid; q < a.ids_stride; q += kSelThreads)
         ids[q] = -1;
