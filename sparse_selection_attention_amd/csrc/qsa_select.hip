@@ -10,9 +10,11 @@
 // rows qsa_attn reads.
 //
 // Design on CDNA4. One workgroup of 512 threads per row (1024 for rows past
-// 16384 cells);
-// the row's scores become order-preserving 32-bit keys held in registers
-// (thread i holds cells i + 512 j, so every read is coalesced):
+// 16384 cells), at most 64 VGPRs so that two rows share a CU; the row's scores
+// become order-preserving 32-bit keys held in registers (thread i holds cells
+// i + NT j, so every read is coalesced; the reads go through a buffer resource
+// sized to the row's causal cells, so one offset register serves them all and
+// cells past the row read zero):
 //   * the K-th largest key is found with four 8-bit radix passes from the top
 //     byte down. The top byte's histogram keeps 32 counters per bin
 //     (bin * 32 + lane % 32), so at most two lanes of a wave add to one
@@ -53,8 +55,11 @@ __device__ inline uint32_t order_key(float f)
     return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
 
-template <int NT, int KPT>      // NT threads per row, KPT keys per thread
-__global__ __launch_bounds__(NT) void select_kernel(SelectArgs a)
+// NT threads per row, KPT keys per thread. Eight waves per SIMD (at most 64
+// VGPRs) let two 1024-thread rows share a CU, so one row's reads overlap the
+// other's histogram passes.
+template <int NT, int KPT>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(8))) void select_kernel(SelectArgs a)
 {
     constexpr int kSelThreads = NT;
     constexpr int kSelWaves = NT / 64;
@@ -77,18 +82,19 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a)
         return;
     }
 
-    const float *row = a.scores + (int64_t)t * a.row_stride;
+    // the row's causal cells through a buffer resource of n * 4 bytes: one
+    // offset register serves every read (the block stride goes in the scalar
+    // offset), and reads past cell p return zero
+    const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(a.scores + (int64_t)t * a.row_stride), 0, n * 4, 0x00020000);
     uint32_t key[KPT];
-    // every read is issued (clamped into the row) before any is used, and the
-    // empty asm keeps the compiler from moving a read under its c < n test,
-    // where each would be waited for on its own; keys replace the raw bits in place
 #pragma unroll
     for (int j = 0; j < KPT; ++j)
-        key[j] = __float_as_uint(row[min(tid + kSelThreads * j, n - 1)]);
+        key[j] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rsrc, tid * 4, kSelThreads * 4 * j, 0);
 #pragma unroll
     for (int j = 0; j < KPT; ++j) {
-        asm volatile("" : "+v"(key[j]));
-        key[j] = tid + kSelThreads * j < n ? order_key(__uint_as_float(key[j])) : 0u;
+        const int lim = n - kSelThreads * j;             // uniform: cell tid + NT j < n iff tid < lim
+        key[j] = tid < lim ? order_key(__uint_as_float(key[j])) : 0u;
     }
 
     // ---- the K-th largest key, one byte at a time ---------------------------
@@ -101,45 +107,10 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a)
     for (int q = tid; q < 3 * kBins; q += kSelThreads)
         cnt1[q] = 0u;
     uint32_t prefix = 0, mask = 0, k_left = (uint32_t)a.K;
-#pragma unroll 1
-    for (int pass = 0; pass < 4; ++pass) {
+    // one wave scans a pass's 256 bin totals from the top for the bin holding
+    // the k_left-th largest candidate; every thread then takes its digit
+    auto pick = [&](const uint32_t *hist, int pass) {
         const int shift = 24 - 8 * pass;
-        const uint32_t *hist;                            // the pass's 256 bin totals
-        if (pass == 0) {
-            for (int q = tid; q < kBins * kCopies / 4; q += kSelThreads)
-                ((uint4 *)cnt)[q] = make_uint4(0u, 0u, 0u, 0u);
-            __syncthreads();
-#pragma unroll
-            for (int j = 0; j < KPT; ++j)
-                atomicAdd(&cnt[(key[j] >> 24) * kCopies + (lane & (kCopies - 1))], 1u);
-            __syncthreads();
-            {   // bin totals: NT / 256 threads per bin, each summing a share of the copies
-                constexpr int kParts = NT / kBins;
-                const int bin = tid / kParts, part = tid % kParts;
-                const uint4 *src = (const uint4 *)(cnt + bin * kCopies + part * (kCopies / kParts));
-                uint32_t sum = 0;
-#pragma unroll
-                for (int i = 0; i < kCopies / 4 / kParts; ++i) {
-                    const uint4 v = src[i];
-                    sum += v.x + v.y + v.z + v.w;
-                }
-#pragma unroll
-                for (int d = 1; d < kParts; d <<= 1)
-                    sum += __shfl_xor(sum, d, 64);
-                if (part == 0)
-                    tot[bin] = sum;
-            }
-            __syncthreads();
-            hist = tot;
-        } else {
-            uint32_t *h = cnt1 + (pass - 1) * kBins;
-#pragma unroll
-            for (int j = 0; j < KPT; ++j)
-                if ((key[j] & mask) == prefix)
-                    atomicAdd(&h[(key[j] >> shift) & 255u], 1u);
-            __syncthreads();
-            hist = h;
-        }
         if (w == 0) {
             // lane l holds bins 4l .. 4l+3; suffix sums from the top bin down
             uint32_t b[4];
@@ -155,7 +126,6 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a)
                     suf += o;
             }
             const uint32_t above_lane = suf - mine;      // bins 4l+4 .. 255
-            // the lane whose bins hold the k_left-th largest candidate
             if (above_lane < k_left && suf >= k_left) {
                 uint32_t acc = above_lane;
                 int digit = 4 * lane + 3;
@@ -176,6 +146,45 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a)
         prefix |= digit << shift;
         mask |= 255u << shift;
         k_left -= acc;
+    };
+
+    // the top byte: every key, 32 counters per bin
+    for (int q = tid; q < kBins * kCopies / 4; q += kSelThreads)
+        ((uint4 *)cnt)[q] = make_uint4(0u, 0u, 0u, 0u);
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < KPT; ++j)
+        atomicAdd(&cnt[(key[j] >> 24) * kCopies + (lane & (kCopies - 1))], 1u);
+    __syncthreads();
+    {   // bin totals: NT / 256 threads per bin, each summing a share of the copies
+        constexpr int kParts = NT / kBins;
+        const int bin = tid / kParts, part = tid % kParts;
+        const uint4 *src = (const uint4 *)(cnt + bin * kCopies + part * (kCopies / kParts));
+        uint32_t sum = 0;
+#pragma unroll
+        for (int i = 0; i < kCopies / 4 / kParts; ++i) {
+            const uint4 v = src[i];
+            sum += v.x + v.y + v.z + v.w;
+        }
+#pragma unroll
+        for (int d = 1; d < kParts; d <<= 1)
+            sum += __shfl_xor(sum, d, 64);
+        if (part == 0)
+            tot[bin] = sum;
+    }
+    __syncthreads();
+    pick(tot, 0);
+    // the lower bytes: only the keys whose higher bytes match the digits so far
+#pragma unroll 1
+    for (int pass = 1; pass < 4; ++pass) {
+        const int shift = 24 - 8 * pass;
+        uint32_t *h = cnt1 + (pass - 1) * kBins;
+#pragma unroll
+        for (int j = 0; j < KPT; ++j)
+            if ((key[j] & mask) == prefix)
+                atomicAdd(&h[(key[j] >> shift) & 255u], 1u);
+        __syncthreads();
+        pick(h, pass);
     }
     const uint32_t tau = prefix;                         // the K-th largest key
     const uint32_t take_eq = k_left;                     // keys equal to tau that are taken (in cell order);
