@@ -115,3 +115,25 @@ def test_score_select_attend_pipeline():
         chosen[sel] = True
         assert not np.any(s_h[t, :p + 1][~chosen] > s_h[t, :p + 1][chosen].min())
     assert torch.isfinite(out.float()).all() and torch.equal(out, out2)
+
+
+@pytest.mark.parametrize("n_in_bin", [0, 1, 4000, 8192, 8193, 20000])
+def test_rows_crowded_into_one_top_byte_bin(n_in_bin):
+    """Rows with 1, 4000, 8192, 8193 and 20000 keys in [1, 2) (one top-byte
+    bin, the rest below it), with repeated values among them, and
+    (n_in_bin = 0) rows whose every key shares one top byte: the threshold is
+    decided by the lower bytes, against the oracle bit for bit."""
+    T, pos0 = 4, 20000
+    rng = np.random.default_rng(n_in_bin + 7)
+    scores = rng.uniform(0.25, 0.5, (T, pos0 + T)).astype(np.float32)
+    pos = rng.choice(pos0, size=n_in_bin, replace=False)
+    vals = rng.uniform(1.0, 2.0, n_in_bin).astype(np.float32)
+    if n_in_bin:
+        vals[::7] = vals[0]                          # runs of one equal value
+    scores[:, pos] = vals
+    for K in (1, 100, 2051, max(1, n_in_bin - 1)):
+        stride = stride_for(K, pos0, T)
+        got = run(scores, pos0, K, stride)
+        want = oracle.select(scores, pos0, K, stride, threads=8)
+        bad = np.argwhere(got != want)
+        assert bad.size == 0, "K=%d first differences (row, slot): %s" % (K, bad[:5].tolist())
