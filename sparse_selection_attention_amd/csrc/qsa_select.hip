@@ -13,8 +13,8 @@
 // 16384 cells), at most 64 VGPRs so that two rows share a CU; the row's scores
 // become order-preserving 32-bit keys held in registers (thread i holds cells
 // i + NT j, so every read is coalesced; the reads go through a buffer resource
-// sized to the row's causal cells, so one offset register serves them all and
-// cells past the row read zero):
+// sized to the row's causal cells, so cells past the row read zero without a
+// clamp):
 //   * the K-th largest key is found with four 8-bit radix passes from the top
 //     byte down. The top byte's histogram keeps 32 counters per bin
 //     (bin * 32 + lane % 32), so at most two lanes of a wave add to one
@@ -82,15 +82,16 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(8))) void se
         return;
     }
 
-    // the row's causal cells through a buffer resource of n * 4 bytes: one
-    // offset register serves every read (the block stride goes in the scalar
-    // offset), and reads past cell p return zero
+    // the row's causal cells through a buffer resource of n * 4 bytes: a read
+    // past cell p returns zero and touches no memory. The whole cell offset
+    // goes in the per-lane offset, which the hardware checks against the
+    // resource's size (the scalar offset is not part of that check).
     const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
         (void *)(a.scores + (int64_t)t * a.row_stride), 0, n * 4, 0x00020000);
     uint32_t key[KPT];
 #pragma unroll
     for (int j = 0; j < KPT; ++j)
-        key[j] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rsrc, tid * 4, kSelThreads * 4 * j, 0);
+        key[j] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rsrc, (tid + kSelThreads * j) * 4, 0, 0);
 #pragma unroll
     for (int j = 0; j < KPT; ++j) {
         const int lim = n - kSelThreads * j;             // uniform: cell tid + NT j < n iff tid < lim
