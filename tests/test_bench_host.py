@@ -1,0 +1,61 @@
+"""Host logic of bench.py: the one-GPU guard, the algorithmic byte counts the
+roofline is computed from, and the rule that a counted traffic figure is used
+only for the kernel source it was taken on."""
+import os
+import subprocess
+import sys
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+from sparse_selection_attention_amd import synth  # noqa: E402
+
+
+def test_more_than_one_gpu_is_refused_with_a_message():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr and r.stdout == ""
+
+
+def test_long_context_algorithmic_bytes():
+    """Per token: 272 B per valid cell (K and V rows, 8 B of scales each), 256 B
+    per chunk of ids, 3072 B of q, and 520 B per (non-empty chunk, head) of
+    records; the merge reads the records and writes 3072 B of output. At the
+    long-context workload (2051 cells in 33 chunks, all non-empty) that is
+    1,538,219,008 B for qsa_attn and 414,640,128 B for qsa_merge."""
+    case = synth.long_ctx(layers=1)
+    a, c = bench.attn_bytes(case.ids, case.n_cells, case.T, case.H, case.D, case.n_chunks)
+    m = bench.merge_bytes(case.T, case.H, case.D, case.n_chunks, c)
+    assert np.all(c == 33)
+    per_token_attn = 2051 * 272 + 256 * 33 + 2 * 12 * 128 + 12 * (8 * 33 + 4 * 128 * 33)
+    per_token_merge = 12 * (8 * 33 + 4 * 128 * 33) + 2 * 12 * 128
+    assert a == 1984 * per_token_attn == 1538219008
+    assert m == 1984 * per_token_merge == 414640128
+
+
+def test_bytes_count_only_valid_cells_and_non_empty_chunks():
+    T, H, D, C, n_cells = 3, 2, 128, 2, 100
+    ids = np.full((T, 64 * C), -1, dtype=np.int32)
+    ids[0, :10] = np.arange(10)                      # 10 cells, one chunk
+    ids[1, 70] = 5                                   # 1 cell in the second chunk
+    ids[1, 71] = n_cells                             # out of range: not a cell
+    a, c = bench.attn_bytes(ids, n_cells, T, H, D, C)
+    assert list(c) == [1, 1, 0]
+    rec = lambda k: H * (8 * C + 4 * D * k)
+    assert a == (10 + 1) * 272 + 3 * (256 * C + 2 * H * D) + rec(1) + rec(1) + rec(0)
+    assert bench.merge_bytes(T, H, D, C, c) == rec(1) + rec(1) + rec(0) + 3 * 2 * H * D
+
+
+def test_traffic_is_read_only_for_the_source_it_was_taken_on(tmp_path):
+    src = tmp_path / "k.hip"
+    src.write_text("kernel v1\n")
+    prof = tmp_path / "p.md"
+    prof.write_text("hbm bytes per launch: 12345\nkernel source sha256: %s\n" % bench.src_hash(str(src)))
+    assert bench.read_traffic(str(prof), [str(src)]) == 12345
+    src.write_text("kernel v2\n")
+    assert bench.read_traffic(str(prof), [str(src)]) is None
+    assert bench.read_traffic(str(tmp_path / "missing.md"), [str(src)]) is None
