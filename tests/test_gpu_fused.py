@@ -135,14 +135,15 @@ def test_fused_large_and_tiny_scales():
         assert np.abs(g - r["out64"]).max() <= 2e-3 * scale_out
 
 
-@pytest.mark.parametrize("C", list(range(1, 11)))
-def test_fused_chunk_counts_and_wave_counts(C):
-    """Rows of 1 to 8 chunks run one wave per chunk, longer rows four waves that
-    each walk several chunks: every token against the oracle, and three runs
+@pytest.mark.parametrize("C,H", [(c, 12) for c in range(1, 11)] + [(8, 16), (8, 1), (9, 16)])
+def test_fused_chunk_counts_and_wave_counts(C, H):
+    """Rows of 1 to 8 chunks run one wave per chunk (8 waves and 16 heads is
+    the largest LDS footprint, about 80 KB), longer rows four waves that each
+    walk several chunks: every token against the oracle, and three runs
     bitwise equal."""
-    L, ids, pos0 = probe_case(T=12, C=C, seed=40 + C)
+    L, ids, pos0 = probe_case(T=12, H=H, C=C, seed=40 + C + H)
     outs = [run_fused(L, ids, pos0, synth.SCALE_1_SQRT_128) for _ in range(3)]
     assert all(np.array_equal(outs[0].view(np.uint16), o.view(np.uint16)) for o in outs[1:])
     refs = oracle_tokens(L, ids, pos0, synth.SCALE_1_SQRT_128, list(range(12)))
     for t, r in refs.items():
-        check_out(outs[0][t], r["out64"], "fused C=%d t=%d" % (C, t))
+        check_out(outs[0][t], r["out64"], "fused C=%d H=%d t=%d" % (C, H, t))
