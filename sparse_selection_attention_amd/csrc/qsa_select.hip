@@ -46,13 +46,14 @@ constexpr int kLDec = kLTot + kBins * 4;               // uint[2][2]: digit, cou
 constexpr int kLCnt1 = kLDec + 16;                     // uint[3 passes][256]: single-copy histograms
 constexpr int kSelLds = kLCnt1 + 3 * kBins * 4;
 
-// Order-preserving key: larger score, larger key; -0 and +0 share one key.
+// Order-preserving key: larger score, larger key. Non-negative scores map to
+// b | 2^31 (+0 to 2^31); negative ones to 2^32 - b, so -0 (b = 2^31) meets
+// +0 at 2^31 and the most negative bit pattern maps to 1, above the key 0
+// that cells past the row get.
 __device__ inline uint32_t order_key(float f)
 {
-    uint32_t b = __float_as_uint(f);
-    if ((b << 1) == 0)
-        b = 0;
-    return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+    const uint32_t b = __float_as_uint(f);
+    return (int32_t)b < 0 ? 0u - b : (b | 0x80000000u);
 }
 
 // NT threads per row, KPT keys per thread. Eight waves per SIMD (at most 64
