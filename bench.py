@@ -277,13 +277,22 @@ def main():
         executed = 3.0 * flops
         score_bytes = (4.0 * sum(case.pos0 + t + 1 for t in range(T))      # causal scores written
                        + 4.0 * sc.n_cells * 128 + 4.0 * T * 12 * 128)      # K and q read once
+        mfma_roof = {"bound": "mfma", "achieved": executed / (us * 1e-6) / 1e12, "peak": BF16_MFMA_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": executed / (us * 1e-6) / 1e12 / BF16_MFMA_PEAK_TFLOPS}
+        hbm_roof = {"bound": "hbm", "achieved": score_bytes / (us * 1e-6) / 1e9, "peak": HBM_PEAK_GBS,
+                    "unit": "GB/s", "frac": score_bytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS}
+        # the binding roofline is the one whose lower bound on the time is larger:
+        # the scores' write at 8 TB/s outlasts the split products at 2.5 PFLOP/s
+        t_mfma = executed / (BF16_MFMA_PEAK_TFLOPS * 1e12)
+        t_hbm = score_bytes / (HBM_PEAK_GBS * 1e9)
         result["companion_score"] = {
             "workload": "qsa_score T=1984 pos0=30000 Hs=12 fp32",
             "avg_us": us,
             "fp32_equivalent_tflops": flops / (us * 1e-6) / 1e12,
             "hbm_gbs": score_bytes / (us * 1e-6) / 1e9,
-            "roofline": {"bound": "mfma", "achieved": executed / (us * 1e-6) / 1e12, "peak": BF16_MFMA_PEAK_TFLOPS,
-                         "unit": "TFLOP/s", "frac": executed / (us * 1e-6) / 1e12 / BF16_MFMA_PEAK_TFLOPS},
+            "roofline": hbm_roof if t_hbm >= t_mfma else mfma_roof,
+            "other_roofline": mfma_roof if t_hbm >= t_mfma else hbm_roof,
+            "lower_bound_us": {"hbm": t_hbm * 1e6, "bf16_mfma": t_mfma * 1e6},
         }
         # selection producer on those scores: K = 2051 ids per row (the long-context selection size)
         K_sel = 2051
