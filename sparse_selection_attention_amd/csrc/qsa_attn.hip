@@ -223,10 +223,11 @@ __device__ inline void chunk_scores(float scale, const WaveLds &L, const half8 (
         for (int r = 0; r < 4; ++r) {
             const int cell = 16 * b + 4 * j + r;
             const uint2 kb = L.ksc[cell];
-            const float sv = scale * ((acc[0][r] * half_bits_to_float(kb.x & 0xffffu) +
-                                       acc[1][r] * half_bits_to_float(kb.x >> 16)) +
-                                      (acc[2][r] * half_bits_to_float(kb.y & 0xffffu) +
-                                       acc[3][r] * half_bits_to_float(kb.y >> 16)));
+            float dot = acc[0][r] * half_bits_to_float(kb.x & 0xffffu);
+            dot = __builtin_fmaf(acc[1][r], half_bits_to_float(kb.x >> 16), dot);
+            dot = __builtin_fmaf(acc[2][r], half_bits_to_float(kb.y & 0xffffu), dot);
+            dot = __builtin_fmaf(acc[3][r], half_bits_to_float(kb.y >> 16), dot);
+            const float sv = scale * dot;
             S[b][r] = ((mask >> cell) & 1ull) ? sv : -INFINITY;
         }
     }

@@ -280,10 +280,11 @@ __global__ __launch_bounds__(kTileThreads * G) void attn_tile_kernel(AttnArgs a,
             for (int r = 0; r < 4; ++r) {
                 const int cell = 16 * b + 4 * j + r;
                 const uint2 kb = *(const uint2 *)(lds + kLKs + cell * 8);
-                const float sv = a.scale * ((acc[0][r] * half_bits_to_float(kb.x & 0xffffu) +
-                                             acc[1][r] * half_bits_to_float(kb.x >> 16)) +
-                                            (acc[2][r] * half_bits_to_float(kb.y & 0xffffu) +
-                                             acc[3][r] * half_bits_to_float(kb.y >> 16)));
+                float dot = acc[0][r] * half_bits_to_float(kb.x & 0xffffu);
+                dot = __builtin_fmaf(acc[1][r], half_bits_to_float(kb.x >> 16), dot);
+                dot = __builtin_fmaf(acc[2][r], half_bits_to_float(kb.y & 0xffffu), dot);
+                dot = __builtin_fmaf(acc[3][r], half_bits_to_float(kb.y >> 16), dot);
+                const float sv = a.scale * dot;
                 S[b][r] = c0 + cell <= lim ? sv : -INFINITY;
             }
         }
