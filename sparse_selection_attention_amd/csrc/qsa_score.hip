@@ -146,12 +146,17 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a, int n_row_tiles
             // every head's read is issued before the first add (one round trip
             // per row, not one per few heads); the adds keep head order
             const float *qr = a.q + (int64_t)t * a.Hs * kD + 4 * c4;
-            // (indexes past Hs re-read the last head, unconditionally, so that no
-            // load is tied to a branch; those values are not added)
+            // (heads go in groups of four, each group behind one uniform branch;
+            // inside a group, indexes past Hs re-read the last head, with no
+            // branch per load; those values are not added)
             float4 v[kMaxHeads];
 #pragma unroll
-            for (int h = 0; h < kMaxHeads; ++h)
-                v[h] = *(const float4 *)(qr + (int64_t)min(h, a.Hs - 1) * kD);
+            for (int h4 = 0; h4 < kMaxHeads; h4 += 4)
+                if (h4 < a.Hs) {                     // uniform: groups of four heads that hold a head
+#pragma unroll
+                    for (int h = h4; h < h4 + 4; ++h)
+                        v[h] = *(const float4 *)(qr + (int64_t)min(h, a.Hs - 1) * kD);
+                }
 #pragma unroll
             for (int h = 0; h < kMaxHeads; ++h)
                 if (h < a.Hs) {
