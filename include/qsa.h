@@ -202,7 +202,8 @@ QSA_API qsa_status qsa_quant_append(const float *k, const float *v, int32_t n_ro
  * scores      fp32 [T][row_stride] (e.g. qsa_score's output); row_stride >= pos0 + T
  * ids         int32 [T][ids_stride]; ids_stride a multiple of 64 holding
  *             min(K, pos0 + T) ids, so the rows feed qsa_attn directly
- * The library supports pos0 + T <= 32768 (QSA_ERR_UNSUPPORTED beyond).
+ * The library supports pos0 + T <= 2^25 (QSA_ERR_UNSUPPORTED beyond); rows of
+ * more than 32768 cells read their scores once per radix pass instead of once.
  */
 QSA_API qsa_status qsa_select(const float *scores, int64_t row_stride, int32_t pos0, int32_t T, int32_t K,
                       int32_t *ids, int32_t ids_stride, void *stream);

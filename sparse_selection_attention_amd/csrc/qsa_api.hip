@@ -345,9 +345,9 @@ qsa_status qsa_select(const float *scores, int64_t row_stride, int32_t pos0, int
         return fail(QSA_ERR_ARG, "qsa_select: negative T (%d) or pos0 (%d)", T, pos0);
     if (K < 1)
         return fail(QSA_ERR_ARG, "qsa_select: K must be >= 1 (got %d)", K);
-    if ((int64_t)pos0 + T > qsa::kMaxSelectCells)
+    if ((int64_t)pos0 + T > qsa::kMaxCells)
         return fail(QSA_ERR_UNSUPPORTED, "qsa_select: rows of at most %d cells (pos0 + T = %lld)",
-                    qsa::kMaxSelectCells, (long long)pos0 + T);
+                    qsa::kMaxCells, (long long)pos0 + T);
     if (row_stride < (int64_t)pos0 + T)
         return fail(QSA_ERR_ARG, "qsa_select: row_stride (%lld) < pos0 + T (%lld)", (long long)row_stride,
                     (long long)pos0 + T);

@@ -61,7 +61,8 @@ struct SelectArgs {
     int32_t *ids;             // [T][ids_stride]
     int32_t ids_stride;
 };
-constexpr int kMaxSelectCells = 1 << 15;   // cells per row the selection kernel holds in registers
+constexpr int kMaxSelectCells = 1 << 15;   // cells per row the selection kernel holds in registers;
+                                            // longer rows (up to kMaxCells) stream their scores
 
 // Part workspace layout: o, then m, then l, each on a 256-byte boundary.
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }

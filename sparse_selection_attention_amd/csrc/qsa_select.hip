@@ -33,6 +33,8 @@
 // Rows of up to 32768 cells (32 keys per thread).
 #include "qsa_internal.h"
 
+#include <algorithm>
+
 namespace qsa {
 namespace {
 
@@ -259,6 +261,184 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(8))) void se
         ids[q] = -1;
 }
 
+// Rows longer than the registers hold (more than 32768 cells): the same four
+// radix passes and the same compaction, but every pass streams the row's
+// scores from memory again (the keys are rebuilt on each read), and the ids
+// are written one 32768-cell segment at a time, with the counts above and
+// equal to the threshold carried from segment to segment.
+constexpr int kStreamThreads = 1024;
+constexpr int kStreamSeg = 32 * kStreamThreads;       // cells per compaction segment
+
+__global__ __launch_bounds__(kStreamThreads) void select_stream_kernel(SelectArgs a)
+{
+    constexpr int kSelThreads = kStreamThreads;
+    constexpr int kSelWaves = kSelThreads / 64;
+    __shared__ __align__(16) uint8_t lds[kSelLds];
+    uint32_t *cnt = (uint32_t *)(lds + kLCnt);
+    uint32_t *tot = (uint32_t *)(lds + kLTot);
+    uint32_t *dec = (uint32_t *)(lds + kLDec);
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, w = tid >> 6;
+    const int t = blockIdx.x;
+    const int n = a.pos0 + t + 1;                       // cells 0 .. p
+    int32_t *ids = a.ids + (int64_t)t * a.ids_stride;
+    if (n <= a.K) {
+        for (int q = tid; q < a.ids_stride; q += kSelThreads)
+            ids[q] = q < n ? q : -1;
+        return;
+    }
+    // the row's causal cells; a read past cell p returns zero and touches no
+    // memory (the whole offset is in the range-checked per-lane offset)
+    const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(a.scores + (int64_t)t * a.row_stride), 0, n * 4, 0x00020000);
+    auto key_at = [&](int c) -> uint32_t {
+        const uint32_t raw = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rsrc, c * 4, 0, 0);
+        return c < n ? order_key(__uint_as_float(raw)) : 0u;
+    };
+
+    uint32_t *cnt1 = (uint32_t *)(lds + kLCnt1);
+    for (int q = tid; q < 3 * kBins; q += kSelThreads)
+        cnt1[q] = 0u;
+    for (int q = tid; q < kBins * kCopies / 4; q += kSelThreads)
+        ((uint4 *)cnt)[q] = make_uint4(0u, 0u, 0u, 0u);
+    uint32_t prefix = 0, mask = 0, k_left = (uint32_t)a.K;
+    __syncthreads();
+    for (int c = tid; c < n; c += kSelThreads)
+        atomicAdd(&cnt[(key_at(c) >> 24) * kCopies + (lane & (kCopies - 1))], 1u);
+    __syncthreads();
+    {   // bin totals: four threads per bin, each summing eight of the copies
+        constexpr int kParts = kSelThreads / kBins;
+        const int bin = tid / kParts, part = tid % kParts;
+        const uint4 *src = (const uint4 *)(cnt + bin * kCopies + part * (kCopies / kParts));
+        uint32_t sum = 0;
+#pragma unroll
+        for (int i = 0; i < kCopies / 4 / kParts; ++i) {
+            const uint4 v = src[i];
+            sum += v.x + v.y + v.z + v.w;
+        }
+#pragma unroll
+        for (int d = 1; d < kParts; d <<= 1)
+            sum += __shfl_xor(sum, d, 64);
+        if (part == 0)
+            tot[bin] = sum;
+    }
+    __syncthreads();
+#pragma unroll 1
+    for (int pass = 0; pass < 4; ++pass) {
+        const int shift = 24 - 8 * pass;
+        const uint32_t *hist = tot;
+        if (pass > 0) {
+            uint32_t *h = cnt1 + (pass - 1) * kBins;
+            for (int c = tid; c < n; c += kSelThreads) {
+                const uint32_t kc = key_at(c);
+                if ((kc & mask) == prefix)
+                    atomicAdd(&h[(kc >> shift) & 255u], 1u);
+            }
+            __syncthreads();
+            hist = h;
+        }
+        if (w == 0) {
+            uint32_t b[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                b[i] = hist[4 * lane + i];
+            const uint32_t mine = b[0] + b[1] + b[2] + b[3];
+            uint32_t suf = mine;
+#pragma unroll
+            for (int d = 1; d < 64; d <<= 1) {
+                const uint32_t o = __shfl_down(suf, d, 64);
+                if (lane + d < 64)
+                    suf += o;
+            }
+            const uint32_t above_lane = suf - mine;
+            if (above_lane < k_left && suf >= k_left) {
+                uint32_t acc = above_lane;
+                int digit = 4 * lane + 3;
+#pragma unroll
+                for (int i = 3; i >= 0; --i) {
+                    if (acc + b[i] >= k_left) {
+                        digit = 4 * lane + i;
+                        break;
+                    }
+                    acc += b[i];
+                }
+                dec[2 * (pass & 1)] = (uint32_t)digit;
+                dec[2 * (pass & 1) + 1] = acc;
+            }
+        }
+        __syncthreads();
+        const uint32_t digit = dec[2 * (pass & 1)], acc = dec[2 * (pass & 1) + 1];
+        prefix |= digit << shift;
+        mask |= 255u << shift;
+        k_left -= acc;
+    }
+    const uint32_t tau = prefix;
+    const uint32_t take_eq = k_left;
+
+    // ids segment by segment: ballot masks in cell order, one scan over the
+    // threads, counts before the segment carried in (gt_run, eq_run)
+    uint4 *words = (uint4 *)cnt;
+    uint32_t *wsum = tot;
+    uint32_t gt_run = 0, eq_run = 0;
+#pragma unroll 1
+    for (int seg = 0; seg < n; seg += kStreamSeg) {
+        {
+            uint32_t glo = 0, ghi = 0, elo = 0, ehi = 0;
+#pragma unroll 4
+            for (int j = 0; j < 32; ++j) {
+                const uint32_t kc = key_at(seg + tid + kSelThreads * j);
+                const uint64_t bg = __ballot(kc > tau), be = __ballot(kc == tau);
+                const bool mine = lane == j;
+                glo = mine ? (uint32_t)bg : glo;
+                ghi = mine ? (uint32_t)(bg >> 32) : ghi;
+                elo = mine ? (uint32_t)be : elo;
+                ehi = mine ? (uint32_t)(be >> 32) : ehi;
+            }
+            if (lane < 32)
+                words[lane * kSelWaves + w] = make_uint4(glo, ghi, elo, ehi);
+        }
+        __syncthreads();
+        const uint4 wd = words[tid >> 1];
+        const uint32_t gt32 = (tid & 1) ? wd.y : wd.x, eq32 = (tid & 1) ? wd.w : wd.z;
+        const uint32_t own = ((uint32_t)__popc(gt32) << 16) | (uint32_t)__popc(eq32);
+        uint32_t inc = own;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const uint32_t o = __shfl_up(inc, d, 64);
+            if (lane >= d)
+                inc += o;
+        }
+        if (lane == 63)
+            wsum[w] = inc;
+        __syncthreads();
+        uint32_t before = inc - own, seg_total = 0;
+        for (int v = 0; v < kSelWaves; ++v) {
+            const uint32_t sv = wsum[v];
+            if (v < w)
+                before += sv;
+            seg_total += sv;
+        }
+        const uint32_t gt_before = gt_run + (before >> 16), eq_before = eq_run + (before & 0xffffu);
+        uint32_t keep = 0, m = eq32;
+        for (uint32_t k = eq_before; k < take_eq && m != 0; ++k) {
+            keep |= m & (0u - m);
+            m &= m - 1;
+        }
+        uint32_t sel = gt32 | keep;
+        uint32_t slot = gt_before + min(eq_before, take_eq);
+        while (sel != 0) {
+            ids[slot++] = seg + 32 * tid + __builtin_ctz(sel);
+            sel &= sel - 1;
+        }
+        gt_run += seg_total >> 16;
+        eq_run += seg_total & 0xffffu;
+        __syncthreads();                                 // words and wave totals are rewritten next segment
+    }
+    for (int q = a.K + tid; q < a.ids_stride; q += kSelThreads)
+        ids[q] = -1;
+}
+
 template <int NT, int KPT>
 hipError_t launch_kpt(const SelectArgs &a, hipStream_t stream)
 {
@@ -266,9 +446,7 @@ hipError_t launch_kpt(const SelectArgs &a, hipStream_t stream)
     return hipGetLastError();
 }
 
-} // namespace
-
-hipError_t launch_select(const SelectArgs &a, hipStream_t stream)
+hipError_t launch_rows(const SelectArgs &a, hipStream_t stream)
 {
     const int n_max = a.pos0 + a.T;
     if (n_max <= 8 * 512)
@@ -277,7 +455,30 @@ hipError_t launch_select(const SelectArgs &a, hipStream_t stream)
         return launch_kpt<512, 16>(a, stream);
     if (n_max <= 32 * 512)
         return launch_kpt<512, 32>(a, stream);
-    return launch_kpt<1024, 32>(a, stream);          // n_max <= 32768, checked by the caller
+    return launch_kpt<1024, 32>(a, stream);
+}
+
+} // namespace
+
+hipError_t launch_select(const SelectArgs &a, hipStream_t stream)
+{
+    // rows of up to 32768 cells keep their keys in registers; longer rows
+    // (the later rows of a long call) stream their scores
+    const int64_t t_split = std::max<int64_t>(0, std::min<int64_t>(a.T, (int64_t)kMaxSelectCells - a.pos0));
+    if (t_split > 0) {
+        SelectArgs r = a;
+        r.T = (int32_t)t_split;
+        const hipError_t e = launch_rows(r, stream);
+        if (e != hipSuccess || t_split == a.T)
+            return e;
+    }
+    SelectArgs r = a;
+    r.scores = a.scores + t_split * a.row_stride;
+    r.ids = a.ids + t_split * (int64_t)a.ids_stride;
+    r.pos0 = a.pos0 + (int32_t)t_split;
+    r.T = a.T - (int32_t)t_split;
+    hipLaunchKernelGGL(select_stream_kernel, dim3(r.T), dim3(kStreamThreads), 0, stream, r);
+    return hipGetLastError();
 }
 
 } // namespace qsa

@@ -83,7 +83,7 @@ int main(void)
     expect(qsa_select(FAKE, 100, 10, 0, 5, FAKE, 64, NULL), QSA_OK, "select T = 0");
     expect(qsa_select(FAKE, 100, 10, 4, 0, FAKE, 64, NULL), QSA_ERR_ARG, "select K = 0");
     expect(qsa_select(FAKE, 200, 100, 4, 100, FAKE, 64, NULL), QSA_ERR_ARG, "select id row too short");
-    expect(qsa_select(FAKE, 40000, 32766, 4, 100, FAKE, 128, NULL), QSA_ERR_UNSUPPORTED, "select row too long");
+    expect(qsa_select(FAKE, 33554440, 33554430, 4, 100, FAKE, 128, NULL), QSA_ERR_UNSUPPORTED, "select row too long");
     expect(qsa_select(FAKE, 13, 10, 4, 5, FAKE, 64, NULL), QSA_ERR_ARG, "select row_stride < pos0 + T");
 
     /* workspace helpers */

@@ -261,7 +261,7 @@ def select(**kw):
     (dict(ids_stride=0), qsa.QSA_ERR_ARG),
     (dict(ids_stride=32), qsa.QSA_ERR_ARG),          # not a multiple of 64
     (dict(K=100, pos0=100, row_stride=200, ids_stride=64), qsa.QSA_ERR_ARG),   # min(K, pos0 + T) = 100 > 64
-    (dict(pos0=32760, T=10, row_stride=40000), qsa.QSA_ERR_UNSUPPORTED),
+    (dict(pos0=2**25 - 5, T=10, row_stride=2**25 + 5), qsa.QSA_ERR_UNSUPPORTED),
     (dict(scores=None), qsa.QSA_ERR_ARG),
     (dict(ids=None), qsa.QSA_ERR_ARG),
     (dict(scores=FAKE + 2), qsa.QSA_ERR_ARG),

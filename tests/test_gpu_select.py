@@ -83,7 +83,7 @@ def test_zero_rows_and_host_checks():
     with pytest.raises(qsa.QsaError):
         qsa.qsa_select(torch.zeros(2, 10, dtype=torch.float32, device="cuda"), 9, 3, ids)   # row_stride < pos0 + T
     with pytest.raises(qsa.QsaError):
-        qsa.qsa_select(torch.zeros(2, 40000, dtype=torch.float32, device="cuda"), 32767, 3, ids)   # too long
+        qsa.qsa_select(torch.zeros(2, 40000, dtype=torch.float32, device="cuda"), 2 ** 25 - 1, 3, ids)   # too long
 
 
 def test_score_select_attend_pipeline():
@@ -137,3 +137,17 @@ def test_rows_crowded_into_one_top_byte_bin(n_in_bin):
         want = oracle.select(scores, pos0, K, stride, threads=8)
         bad = np.argwhere(got != want)
         assert bad.size == 0, "K=%d first differences (row, slot): %s" % (K, bad[:5].tolist())
+
+
+@pytest.mark.parametrize("kind", synth.SCORE_KINDS)
+@pytest.mark.parametrize("T,pos0,K", [(20, 32760, 2051), (3, 70000, 4000), (2, 131000, 2051), (2, 40000, 45000)])
+def test_rows_past_the_register_limit(kind, T, pos0, K):
+    """Rows of more than 32768 cells stream their scores on every pass; a call
+    whose rows straddle 32768 cells runs both kernels. Every id and pad against
+    the oracle, bit for bit (the last case has K above some rows' length)."""
+    scores = synth.select_scores(T, pos0, seed=T + K + pos0 % 97, kind=kind)
+    stride = stride_for(K, pos0, T)
+    got = run(scores, pos0, K, stride)
+    want = oracle.select(scores, pos0, K, stride, threads=8)
+    bad = np.argwhere(got != want)
+    assert bad.size == 0, "first differences (row, slot): %s" % bad[:5].tolist()
