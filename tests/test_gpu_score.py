@@ -112,3 +112,10 @@ def test_infinite_and_nan_operands():
     assert np.isnan(g[50, : pos0 + 51]).all()
     assert (g[[0, 20, 65], 17] == np.inf).all()
     _compare_causal(sc, g, [0, 3, 17, 20, 40, 50, 65])
+
+
+@pytest.mark.parametrize("T,pos0,Hs", [(1, 30000, 12), (8, 30000, 12), (16, 4000, 3), (17, 4000, 1)])
+def test_decode_sized_score_calls(T, pos0, Hs):
+    """Calls of a few rows (a decode step) spread one column tile per
+    workgroup; every row against the oracle, tail and untouched cells included."""
+    print("score decode-sized", check_score_case(synth.score_case(T=T, pos0=pos0, Hs=Hs), n_sample=T), flush=True)
