@@ -135,15 +135,34 @@ def test_fused_large_and_tiny_scales():
         assert np.abs(g - r["out64"]).max() <= 2e-3 * scale_out
 
 
-@pytest.mark.parametrize("C,H", [(c, 12) for c in range(1, 11)] + [(8, 16), (8, 1), (9, 16)])
-def test_fused_chunk_counts_and_wave_counts(C, H):
+@pytest.mark.parametrize("C,H,T", [(c, 12, 12) for c in range(1, 11)] + [(8, 16, 12), (8, 1, 12), (9, 16, 12)]
+                         + [(9, 12, 65), (11, 16, 65), (17, 3, 64), (17, 3, 65)])
+def test_fused_chunk_counts_and_wave_counts(C, H, T):
     """Rows of 1 to 8 chunks run one wave per chunk (8 waves and 16 heads is
-    the largest LDS footprint, about 80 KB), longer rows four waves that each
-    walk several chunks: every token against the oracle, and three runs
-    bitwise equal."""
-    L, ids, pos0 = probe_case(T=12, H=H, C=C, seed=40 + C + H)
+    the largest LDS footprint, about 80 KB); longer rows run eight waves that
+    each walk several chunks in calls of at most 64 tokens, four waves in
+    larger calls: sampled tokens against the oracle, and three runs bitwise
+    equal."""
+    L, ids, pos0 = probe_case(T=T, H=H, C=C, seed=40 + C + H + T)
     outs = [run_fused(L, ids, pos0, synth.SCALE_1_SQRT_128) for _ in range(3)]
     assert all(np.array_equal(outs[0].view(np.uint16), o.view(np.uint16)) for o in outs[1:])
-    refs = oracle_tokens(L, ids, pos0, synth.SCALE_1_SQRT_128, list(range(12)))
+    toks = list(range(12)) + [T - 2, T - 1] if T > 12 else list(range(T))
+    refs = oracle_tokens(L, ids, pos0, synth.SCALE_1_SQRT_128, toks)
     for t, r in refs.items():
-        check_out(outs[0][t], r["out64"], "fused C=%d H=%d t=%d" % (C, H, t))
+        check_out(outs[0][t], r["out64"], "fused C=%d H=%d T=%d t=%d" % (C, H, T, t))
+
+
+@pytest.mark.parametrize("T", [1, 8, 64, 65])
+def test_fused_long_selection_small_calls(T):
+    """Decode-sized calls over 2051 selected cells (33 chunks) at pos0 = 30000:
+    eight waves walk the chunks up to 64 tokens, four from 65; against the
+    oracle, and two runs bitwise equal."""
+    case = synth.long_ctx(layers=1, T=T)
+    L = case.layers[0]
+    a = run_fused(L, case.ids, case.pos0, case.scale)
+    b = run_fused(L, case.ids, case.pos0, case.scale)
+    assert np.array_equal(a.view(np.uint16), b.view(np.uint16))
+    toks = sorted({0, T // 2, T - 1})
+    refs = oracle_tokens(L, case.ids, case.pos0, case.scale, toks)
+    for t, r in refs.items():
+        check_out(a[t], r["out64"], "fused long T=%d t=%d" % (T, t))
