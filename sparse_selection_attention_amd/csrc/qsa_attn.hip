@@ -56,8 +56,8 @@ namespace {
 
 using namespace dev;
 
-constexpr int kWaves = kAttnWaves;         // waves of a fused workgroup over many chunks
-constexpr int kWavesMax = 8;               // waves of a fused workgroup over few chunks: one each
+constexpr int kWaves = kAttnWaves;         // waves of a fused workgroup over many chunks in a large call
+constexpr int kWavesMax = 8;               // over few chunks (one wave each), or many chunks in a small call
 
 // LDS layout: one wave region per wave, then (fused workgroup only) the q rows
 constexpr int kKTileBytes = kChunk * kD;                 // 8 KB of K rows per wave

@@ -11,7 +11,7 @@ constexpr int kD = 128;       // the one head dim the kernels implement
 constexpr int kChunk = 64;    // slots per chunk
 constexpr int kGroup = 32;    // dims per fp16 scale
 constexpr int kMaxHeads = 16; // heads fill the 16-wide MFMA tile dimension
-constexpr int kAttnWaves = 4; // waves of a fused attention workgroup (one token) over more than 8 chunks
+constexpr int kAttnWaves = 4; // waves of a fused attention workgroup (one token) over more than 8 chunks, in calls of more than 64 tokens
 constexpr int kMaxCells = 1 << 25; // cache rows addressed with 32-bit byte offsets
 
 struct AttnArgs {
