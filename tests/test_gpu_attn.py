@@ -370,3 +370,21 @@ def test_stream_argument_is_honoured():
     s.synchronize()
     ref, _, _ = oracle.attn(L.q, L.kq, L.vq, L.ksc, L.vsc, case.ids, 0, case.scale)
     check_out(out.cpu().numpy(), ref, "stream")
+
+
+@pytest.mark.parametrize("C", [0, 3])
+def test_merge_rows_without_records_give_plus_zero(C):
+    """A row with no finite chunk maximum -- no chunks at all, or only empty-chunk
+    records (m = -inf, l = +0, o holding NaN bytes) -- merges to +0 in every
+    dim, whatever the output held before."""
+    T, H, D = 5, 12, 128
+    part = qsa.alloc_part(T, H, D, C)
+    part.fill_(0xFF)                         # every o float a NaN
+    if C:
+        o, m, l = qsa.part_views(part, T, H, D, C)
+        m.fill_(float("-inf"))
+        l.zero_()
+    out = torch.full((T, H, D), float("nan"), dtype=torch.float16, device="cuda")
+    qsa.qsa_merge(part, C, out)
+    torch.cuda.synchronize()
+    assert np.all(out.cpu().numpy().view(np.uint16) == 0)
