@@ -123,7 +123,8 @@ QSA_API qsa_status qsa_attn_merge(const void *q, const int8_t *kq, const int8_t 
  * h, over chunks with m_k != -inf:
  *   M = max_k m_k,  w_k = exp(m_k - M),  L = sum_k w_k l_k,
  *   out[t][h][d] = fp16_rne( sum_k w_k o_k[d] / L )
- * A (t, h) with no such chunk gets +0 in every dim. Records with m = -inf are
+ * A (t, h) with no such chunk gets +0 in every dim; so does every row when
+ * n_chunks is 0, and then part is not read. Records with m = -inf are
  * skipped and their o is never read.
  *
  * part     records written by qsa_attn with the same T, H, D and n_chunks
