@@ -55,6 +55,10 @@ def lib():
         L.qso_quant_rows.restype = _ct.c_int
         L.qso_select.argtypes = [P, _ct.c_int64, i32, i32, i32, P, i32, i32, i32]
         L.qso_select.restype = _ct.c_int
+        L.qso_gate.argtypes = [P, P, _ct.c_int64, P, P]
+        L.qso_gate.restype = _ct.c_int
+        L.qso_sums16.argtypes = [P, _ct.c_int64, i32, P]
+        L.qso_sums16.restype = _ct.c_int
         _lib = L
     return _lib
 
@@ -194,3 +198,42 @@ def select(scores, pos0, K, ids_stride, t_range=None, threads=1):
 
     _run_ranges(run, _ranges(t0, t1, threads))
     return ids
+
+
+def gate(y64, g):
+    """Sigmoid-gated output (qso_gate): y64 fp64 merged values, g fp32 gates of
+    the same shape. Returns (out64 fp64, out16 fp16)."""
+    y64 = _np.ascontiguousarray(y64, dtype=_np.float64)
+    g = _np.ascontiguousarray(g, dtype=_np.float32)
+    if y64.shape != g.shape:
+        raise ValueError("gates must have the output's shape")
+    out64 = _np.empty_like(y64)
+    out16 = _np.empty(y64.shape, dtype=_np.uint16)
+    if lib().qso_gate(_ptr(y64), _ptr(g), y64.size, _ptr(out64), _ptr(out16)) != 0:
+        raise ValueError("qso_gate: bad arguments")
+    return out64, out16.view(_np.float16)
+
+
+def sums16(x16):
+    """Per-16 sums (qso_sums16) of fp16 values [..., D]: float32 [..., D/16]."""
+    x16 = _np.ascontiguousarray(x16, dtype=_np.float16)
+    D = x16.shape[-1]
+    rows = x16.size // D
+    out = _np.empty(x16.shape[:-1] + (D // 16,), dtype=_np.float32)
+    if lib().qso_sums16(_ptr(x16.view(_np.uint16)), rows, D, _ptr(out)) != 0:
+        raise ValueError("qso_sums16: bad arguments")
+    return out
+
+
+def attn_gated(q, kq, vq, ksc, vsc, ids, pos0, scale, g, t_range=None, threads=1):
+    """Whole gated path: chunk records, merge, sigmoid gate, per-16 sums.
+    Returns (out64, out16, sums) for the tokens in t_range (other rows NaN)."""
+    y64, _, _ = attn(q, kq, vq, ksc, vsc, ids, pos0, scale, t_range=t_range, threads=threads)
+    t0, t1 = (0, q.shape[0]) if t_range is None else t_range
+    out64 = _np.full(y64.shape, _np.nan)
+    out16 = _np.full(y64.shape, _np.nan, dtype=_np.float16)
+    sums = _np.full(y64.shape[:-1] + (y64.shape[-1] // 16,), _np.nan, dtype=_np.float32)
+    a, b = gate(y64[t0:t1], g[t0:t1])
+    out64[t0:t1], out16[t0:t1] = a, b
+    sums[t0:t1] = sums16(b)
+    return out64, out16, sums

@@ -65,6 +65,26 @@
  *    scores[t][c], equal scores (-0 equal to +0) going to the smaller cell
  *    index, written in ascending cell order and padded with -1 to ids_stride.
  *    Scores must not be NaN.
+ *  qso_gate -- the sigmoid gate on the merged output. The pages say the fused
+ *    decode kernel keeps the sigmoid gate ("round 5 track b: cached residual
+ *    norms and fused mtp attention", section "preflight / ownership") and that
+ *    gates, like queries, are fp32 inputs (same page, section "actual
+ *    verification"); they do not print its shape. The reading taken is one
+ *    fp32 gate g per output element [T][H][D]:
+ *      out = sigmoid(g) * y,  sigmoid(g) = 1 / (1 + exp(-g)),
+ *    where y is the merged value O / L (before any rounding), rounded once to
+ *    binary16 by round-to-nearest-even. IEEE rules decide the edges: g = +inf
+ *    gives y, g = -inf gives a zero with y's sign, a NaN gate gives NaN.
+ *  qso_sums16 -- per-16 sums of the written output. The same page lists the
+ *    per-16 sums among what the fused kernel must keep and compares them byte
+ *    for byte (sections "preflight / ownership", "mtp attention" and "actual
+ *    verification"), without saying what is summed or in which tree. The
+ *    reading taken: for each row of binary16 outputs and each block of 16
+ *    consecutive values, the exact sum of the 16 values rounded once to
+ *    binary32 (nearest, ties to even). Every binary16 value is an integer
+ *    multiple of 2^-24 below 2^16, so 16 of them sum exactly in binary64
+ *    (< 2^44 units of 2^-24) in any order, and the result depends on no
+ *    summation tree.
  */
 #include <math.h>
 #include <stddef.h>
@@ -373,5 +393,47 @@ int qso_select(const float *scores, int64_t row_stride, int32_t pos0, int32_t T,
             row[j] = j < take ? order[j] : -1;
     }
     free(order);
+    return 0;
+}
+
+/* ---- sigmoid gate and per-16 sums ---------------------------------------------- */
+
+/*
+ * Gated output for n values: out64[i] = y[i] / (1 + exp(-gate[i])), i.e.
+ * sigmoid(gate[i]) * y[i], and out16[i] its binary16 rounding (either output
+ * may be NULL).
+ */
+int qso_gate(const double *y, const float *gate, int64_t n, double *out64, uint16_t *out16)
+{
+    if (n < 0)
+        return -1;
+    for (int64_t i = 0; i < n; ++i) {
+        double sig = 1.0 / (1.0 + exp(-(double)gate[i]));
+        double v = sig * y[i];
+        if (out64)
+            out64[i] = v;
+        if (out16)
+            out16[i] = qso_double_to_half(v);
+    }
+    return 0;
+}
+
+/*
+ * Per-16 sums of n_rows rows of D binary16 values (D a multiple of 16):
+ * sums[r][b] = binary32 rounding of the exact sum of x[r][16b .. 16b + 15].
+ * The binary64 running sum below is exact (see the header), so the one
+ * rounding is the conversion to float.
+ */
+int qso_sums16(const uint16_t *x, int64_t n_rows, int32_t D, float *sums)
+{
+    if (n_rows < 0 || D <= 0 || D % 16 != 0)
+        return -1;
+    for (int64_t r = 0; r < n_rows; ++r)
+        for (int32_t b = 0; b < D / 16; ++b) {
+            double acc = 0.0;
+            for (int i = 0; i < 16; ++i)
+                acc += qso_half_to_double(x[r * D + 16 * b + i]);
+            sums[r * (D / 16) + b] = (float)acc;
+        }
     return 0;
 }

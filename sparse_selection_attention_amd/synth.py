@@ -36,6 +36,7 @@ _MASK = (1 << 64) - 1
 TID_Q, TID_KQ, TID_VQ, TID_KSC, TID_VSC, TID_SCORE_Q, TID_SCORE_K, TID_EDGE = range(8)
 TID_ROWS, TID_ROWS_MAG, TID_ROWS_INT = range(8, 11)
 TID_SEL, TID_SEL_INT = range(11, 13)
+TID_GATE = 13
 
 HEAD_DIM = 128
 GROUP = 32          # one fp16 scale per 32 consecutive dims of a cached row
@@ -398,3 +399,27 @@ def select_scores(T: int, pos0: int, seed: int = 5, kind: str = "normal", row_st
     p = pos0 + np.arange(T)[:, None]
     x[cols > p] = np.float32(3e38)
     return np.ascontiguousarray(x)
+
+
+# ---------------------------------------------------------------------------
+# output gates
+
+
+GATE_KINDS = ("normal", "special")
+
+
+def gates(T: int, H: int, seed: int = 5, layer: int = 0, kind: str = "normal", D: int = HEAD_DIM) -> np.ndarray:
+    """fp32 gate inputs [T][H][D], one per output element.
+
+    "normal": N(0, 2^2), so the sigmoid runs from about 0.002 to 0.998;
+    "special": the same draws with every 7th element replaced, in turn, by 0,
+    +inf, -inf, +100, -100, -0.0, 1e-30 and -1e-30.
+    """
+    if kind not in GATE_KINDS:
+        raise ValueError(kind)
+    g = (2.0 * normal(stream_key(seed, layer, TID_GATE), T * H * D)).astype(np.float32)
+    if kind == "special":
+        picks = np.array([0.0, math.inf, -math.inf, 100.0, -100.0, -0.0, 1e-30, -1e-30], dtype=np.float32)
+        idx = np.arange(0, g.size, 7)
+        g[idx] = picks[np.arange(idx.size) % picks.size]
+    return g.reshape(T, H, D)

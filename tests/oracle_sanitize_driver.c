@@ -8,8 +8,9 @@
  * Cases: poisoned slots (-1, negative, at and past n_cells), an empty chunk, a
  * row with no valid slot, a ragged last chunk, implicit all-causal rows,
  * scores with a clipped dead-key tail, quantisation of zero, huge, subnormal
- * and tied groups, selection with K above and below the row length, and
- * rejected shapes.
+ * and tied groups, selection with K above and below the row length, gates at
+ * 0, +-inf, +-100 and NaN on outputs at the binary16 limits, per-16 sums over
+ * infinities and signed zeros, and rejected shapes.
  */
 #include <math.h>
 #include <stdint.h>
@@ -30,6 +31,8 @@ int qso_score(const float *q, const float *k, int32_t n_cells, int32_t pos0, int
 int qso_quant_rows(const float *x, int32_t n_rows, int32_t D, int8_t *codes, uint16_t *scales);
 int qso_select(const float *scores, int64_t row_stride, int32_t pos0, int32_t T, int32_t K, int32_t *ids,
                int32_t ids_stride, int32_t t_begin, int32_t t_end);
+int qso_gate(const double *y, const float *gate, int64_t n, double *out64, uint16_t *out16);
+int qso_sums16(const uint16_t *x, int64_t n_rows, int32_t D, float *sums);
 
 static uint64_t rng_state = 0x9e3779b97f4a7c15ull;
 static uint32_t next_u32(void)
@@ -184,6 +187,34 @@ static void select_cases(void)
     free(s);
 }
 
+static void gate_cases(void)
+{
+    const int n = 12;
+    const double y[12] = {1.0, -1.0, 0.0, -0.0, 65504.0, -65504.0, 1e5, 3e-8, 0.25, -0.75, 7.0, 2.0};
+    const float g[12] = {0.0f, 0.0f, 1.0f, -1.0f, INFINITY, -INFINITY, 100.0f, -100.0f, NAN, 2.5f, -2.5f, 1e-30f};
+    double out64[12];
+    uint16_t out16[12];
+    CHECK(qso_gate(y, g, n, out64, out16) == 0, "gate");
+    CHECK(out64[0] == 0.5 && out64[1] == -0.5, "sigmoid(0) halves");
+    CHECK(out64[4] == 65504.0 && out16[4] == 0x7bff, "sigmoid(+inf) keeps the value");
+    CHECK(out64[5] == 0.0 && signbit(out64[5]), "sigmoid(-inf) gives a zero of the value's sign");
+    CHECK(out64[8] != out64[8], "NaN gate gives NaN");
+    CHECK(qso_gate(y, g, n, NULL, NULL) == 0, "gate with no outputs");
+    CHECK(qso_gate(y, g, -1, out64, out16) != 0, "gate rejects n < 0");
+
+    uint16_t x[3 * 32];
+    for (int i = 0; i < 3 * 32; ++i)
+        x[i] = (uint16_t)(next_u32() & 0xffffu);
+    for (int i = 0; i < 16; ++i)
+        x[i] = (uint16_t)(i & 1 ? 0x8000u : 0x0000u);   /* signed zeros only */
+    x[20] = 0x7c00u;                                     /* +inf */
+    x[21] = 0xfc00u;                                     /* -inf */
+    float sums[3 * 2];
+    CHECK(qso_sums16(x, 3, 32, sums) == 0, "sums16");
+    CHECK(sums[0] == 0.0f, "sum of signed zeros");
+    CHECK(qso_sums16(x, 3, 24, sums) != 0, "sums16 rejects D % 16 != 0");
+}
+
 int main(void)
 {
     for (uint32_t b = 0; b < 65536u; ++b) {          /* every binary16 value through both conversions */
@@ -195,6 +226,7 @@ int main(void)
     score_cases();
     quant_cases();
     select_cases();
+    gate_cases();
     if (fails) {
         fprintf(stderr, "%d driver checks failed\n", fails);
         return 1;
