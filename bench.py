@@ -7,12 +7,14 @@ up to 2051 evenly spaced causal cells per token in 33 chunks, 3 independent
 layers, seed 5. One step is qsa_attn + qsa_merge for each of the 3 layers on
 one stream, with every input resident in HBM before the timed region.
 
-Prints one JSON line: query-token*heads per second, achieved algorithmic GB/s,
-the roofline of the dominant kernel (qsa_attn) measured with HIP events inside
-the timed region, the single-dispatch attention + merge, the companion
-causal-score kernel, the selection producer on its output, the int8 cache
-writer, the shared-tile prompt path, and the CPU oracle timed on a bounded
-sample on this host's cores.
+Prints one JSON line: query-token*heads per second (whole timed region, and
+the median step), per-step median / min / max from HIP events, a cold-cache
+sample (the caches scrubbed before each step), the HBM roofline of the
+dominant kernel (qsa_attn) with its counted traffic, the single-dispatch
+attention + merge, the gated output, the companion causal-score kernel, the
+selection producer on its output, the int8 cache writer, the shared-tile
+prompt path, the decode window, and the CPU oracle timed on bounded samples
+on this host's cores.
 """
 from __future__ import annotations
 
@@ -48,6 +50,18 @@ def attn_bytes(ids, n_cells, T, H, D, C):
     return int(per.sum()), c
 
 
+def attn_min_bytes(ids, n_cells, T, H, D, C):
+    """Fewest HBM bytes one qsa_attn launch can move: every selected cell's K
+    and V rows and scales once (however many tokens select it), every id slot,
+    q, and the chunk records written. This is the per-token count with the
+    K/V term taken per distinct cell of the launch."""
+    import numpy as np
+    v = (ids >= 0) & (ids < n_cells)
+    uniq = int(np.unique(ids[v]).size)
+    c = v.reshape(T, C, 64).any(axis=2).sum(axis=1)
+    return uniq * (2 * D + 2 * 2 * (D // 32)) + 4 * 64 * C * T + 2 * H * D * T + int((H * (8 * C + 4 * D * c)).sum())
+
+
 def merge_bytes(T, H, D, C, c):
     # reads (m, l) of every chunk and o of non-empty chunks, writes fp16 out
     return int((H * 8 * C + H * 4 * D * c + 2 * H * D).sum()) if hasattr(c, "sum") else None
@@ -79,24 +93,68 @@ def read_traffic(profile_md, kernel_srcs):
     return int(m_bytes.group(1))
 
 
-def cpu_baseline(case, out_gpu, n_tokens, threads):
-    """The oracle, as it stands, on a sample of layer-0 tokens, spread over host cores."""
-    import numpy as np
+def host_cpu():
+    """(worker threads for the oracle, logical CPUs this process may run on, CPU model).
+
+    The oracle's worker pool takes the CPU share the host gives this process:
+    OMP_NUM_THREADS when it is set (the share of one GPU on a shared GPU host),
+    else every CPU in the affinity mask."""
+    visible = len(os.sched_getaffinity(0))
+    try:
+        share = int(os.environ.get("OMP_NUM_THREADS", "0"))
+    except ValueError:
+        share = 0
+    threads = max(1, min(visible, share)) if share > 0 else visible
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return threads, visible, model
+
+
+def _oracle_tokens(case, L, toks, threads):
+    """Oracle output of the given tokens, one token per task, on `threads` host threads."""
     import oracle
 
-    L = case.layers[0]
-    toks = np.linspace(0, case.T - 1, n_tokens).astype(int).tolist()
-
     def one(t):
-        m, l, o = oracle.attn_chunks(L.q[t: t + 1], L.kq, L.vq, L.ksc, L.vsc, case.ids[t: t + 1],
-                                     case.pos0 + t, case.scale)
+        ids = None if case.ids is None else case.ids[t: t + 1]
+        m, l, o = oracle.attn_chunks(L.q[t: t + 1], L.kq, L.vq, L.ksc, L.vsc, ids, case.pos0 + t, case.scale)
         return oracle.merge(m, l, o)[0][0]
 
     t0 = time.perf_counter()
-    with cf.ThreadPoolExecutor(threads) as ex:
-        res = list(ex.map(one, toks))
-    dt = time.perf_counter() - t0
+    if threads == 1:
+        res = [one(t) for t in toks]
+    else:
+        with cf.ThreadPoolExecutor(threads) as ex:
+            res = list(ex.map(one, toks))
+    return res, time.perf_counter() - t0
+
+
+def cpu_baseline(case, out_gpu, n_tokens, single_tokens):
+    """The oracle, as it stands, on bounded samples of the benchmark's workload
+    (and single-thread on the tiny and decode-window workloads), on this host."""
+    import numpy as np
+    from sparse_selection_attention_amd import synth
+
+    threads, visible, model = host_cpu()
+    L = case.layers[0]
+    toks = np.linspace(0, case.T - 1, n_tokens).astype(int).tolist()
+    res, dt = _oracle_tokens(case, L, toks, threads)
     err = max(float(np.abs(out_gpu[t].astype(np.float64) - r).max()) for t, r in zip(toks, res))
+    # one thread: a smaller sample of the same layer, and two whole small workloads
+    stoks = np.linspace(0, case.T - 1, single_tokens).astype(int).tolist()
+    _, dt1 = _oracle_tokens(case, L, stoks, 1)
+    single = {"long_context_layer_sample": {
+        "tokens": single_tokens, "seconds": dt1, "query-token*heads/s": single_tokens * case.H / dt1,
+        "projected_seconds_per_layer": dt1 * case.T / single_tokens}}
+    for name, small in (("tiny", synth.tiny()), ("decode_window_8_tokens", synth.mtp(8))):
+        _, dts = _oracle_tokens(small, small.layers[0], list(range(small.T)), 1)
+        single[name] = {"tokens": small.T, "heads": small.H, "seconds": dts,
+                        "query-token*heads/s": small.T * small.H / dts}
     return {
         "value": n_tokens * case.H / dt,
         "unit": "query-token*heads/s",
@@ -104,8 +162,48 @@ def cpu_baseline(case, out_gpu, n_tokens, threads):
         "kind": "oracle",
         "sample": "%d evenly spaced tokens of layer 0 of the same workload (fp64 C oracle, %d threads, %.1f s wall)"
                   % (n_tokens, threads, dt),
+        "host": {"cpu_model": model, "logical_cpus_visible": visible, "threads_used": threads,
+                 "why": "the oracle's pool takes this process's CPU share (OMP_NUM_THREADS when set, else the "
+                        "affinity mask)"},
+        "single_thread": single,
         "max_abs_diff_vs_gpu": err,
     }
+
+
+def score_errors(sc, scores_gpu, n_rows, threads):
+    """Largest score error on sampled rows, against the oracle, as err / A (A the
+    dot product's error scale |scale| sum_d |sum_h q_d| |k_d|) and as err / |r|
+    over cells with r != 0."""
+    import numpy as np
+    import oracle
+
+    rows = np.linspace(0, sc.T - 1, n_rows).astype(int).tolist()
+    qs = np.abs(sc.q.astype(np.float64).sum(axis=1))
+    kabs = np.abs(sc.k.astype(np.float64))
+
+    def one(t):
+        r = oracle.score(sc.q[t: t + 1], sc.k, sc.pos0 + t, sc.scale, sc.dead, sc.row_stride)[0]
+        p = sc.pos0 + t
+        g = scores_gpu[t, : p + 1].astype(np.float64)
+        err = np.abs(g - r[: p + 1])
+        A = abs(float(sc.scale)) * (kabs[: p + 1] @ qs[t])
+        nz = r[: p + 1] != 0
+        return float((err / A).max()), float((err[nz] / np.abs(r[: p + 1][nz])).max()), \
+            float(np.mean(err[nz] > 1e-4 * np.abs(r[: p + 1][nz])))
+
+    with cf.ThreadPoolExecutor(threads) as ex:
+        res = list(ex.map(one, rows))
+    return {"rows_sampled": n_rows, "max_err_over_A": max(r[0] for r in res),
+            "max_err_over_abs_r": max(r[1] for r in res),
+            "fraction_of_cells_above_1e-4_of_abs_r": float(np.mean([r[2] for r in res])),
+            "note": "A = |scale| sum_d |sum_h q[t][h][d]| |k[c][d]|; the bar is err <= 1e-4 max(|r|, A)"}
+
+
+def stats(xs):
+    import numpy as np
+    xs = np.asarray(xs, dtype=np.float64)
+    return {"n": int(xs.size), "median": float(np.median(xs)), "min": float(xs.min()), "max": float(xs.max()),
+            "mean": float(xs.mean())}
 
 
 def main():
@@ -114,7 +212,10 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--layers", type=int, default=3)
+    ap.add_argument("--cold-samples", type=int, default=9,
+                    help="steps timed after scrubbing L2 and the Infinity Cache (0 to skip)")
     ap.add_argument("--cpu-tokens", type=int, default=384)
+    ap.add_argument("--cpu-single-tokens", type=int, default=96)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
     ap.add_argument("--no-score", action="store_true", help="skip the companion score kernel")
     ap.add_argument("--no-fused", action="store_true", help="skip the single-dispatch attention + merge line")
@@ -153,18 +254,23 @@ def main():
     scale = float(case.scale)
 
     a_bytes, c_nonempty = attn_bytes(case.ids, case.n_cells, T, H, D, C)
+    a_min = attn_min_bytes(case.ids, case.n_cells, T, H, D, C)
     m_bytes = merge_bytes(T, H, D, C, c_nonempty)
 
-    def step(ev=None):
+    def ev():
+        return torch.cuda.Event(enable_timing=True)
+
+    def step(e=None):
+        # e: per layer [start, after attn, after merge] events on the launch stream
         for li, (q, kq, vq, ksc, vsc) in enumerate(layers):
-            if ev is not None:
-                ev[li][0].record(stream)
+            if e is not None:
+                e[li][0].record(stream)
             qsa.qsa_attn(q, kq, vq, ksc, vsc, ids, case.pos0, scale, part, stream=stream)
-            if ev is not None:
-                ev[li][1].record(stream)
+            if e is not None:
+                e[li][1].record(stream)
             qsa.qsa_merge(part, C, outs[li], stream=stream)
-            if ev is not None:
-                ev[li][2].record(stream)
+            if e is not None:
+                e[li][2].record(stream)
 
     print("bench: warmup", file=sys.stderr, flush=True)
     for _ in range(max(1, args.warmup)):
@@ -172,29 +278,29 @@ def main():
     torch.cuda.synchronize()
 
     print("bench: timing %d steps" % args.steps, file=sys.stderr, flush=True)
-    evs = [[[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.layers)]
-           for _ in range(args.steps)]
+    evs = [[[ev() for _ in range(3)] for _ in range(args.layers)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for s in range(args.steps):
-        step(evs[s])
+    for s_ in range(args.steps):
+        step(evs[s_])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    attn_ms = [evs[s][li][0].elapsed_time(evs[s][li][1]) for s in range(args.steps) for li in range(args.layers)]
-    merge_ms = [evs[s][li][1].elapsed_time(evs[s][li][2]) for s in range(args.steps) for li in range(args.layers)]
-    step_ms = [evs[s][0][0].elapsed_time(evs[s][-1][2]) for s in range(args.steps)]
+    attn_us = [1e3 * evs[s_][li][0].elapsed_time(evs[s_][li][1]) for s_ in range(args.steps) for li in range(args.layers)]
+    merge_us = [1e3 * evs[s_][li][1].elapsed_time(evs[s_][li][2]) for s_ in range(args.steps) for li in range(args.layers)]
+    step_ms = [evs[s_][0][0].elapsed_time(evs[s_][-1][2]) for s_ in range(args.steps)]
     ms_per_step = wall * 1e3 / args.steps
+    work = T * H * args.layers
 
-    attn_avg_s = float(np.mean(attn_ms)) * 1e-3
-    merge_avg_s = float(np.mean(merge_ms)) * 1e-3
-    attn_gbs = a_bytes / attn_avg_s / 1e9
+    attn_avg_s = float(np.mean(attn_us)) * 1e-6
+    merge_avg_s = float(np.mean(merge_us)) * 1e-6
     step_bytes = args.layers * (a_bytes + m_bytes)
     traffic = read_traffic(os.path.join(ROOT, "profiles", "qsa_kernels_hbm_counters_bench_workloads.md"),
                            attn_sources())
+    achieved = a_min / attn_avg_s / 1e9
 
     result = {
         "metric": "query-token*heads/sec + achieved HBM GB/s, T=1984 pos0=30000 attention",
-        "value": T * H * args.layers / (ms_per_step * 1e-3),
+        "value": work / (ms_per_step * 1e-3),
         "unit": "query-token*heads/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -213,49 +319,99 @@ def main():
             "T": T, "pos0": case.pos0, "heads": H, "head_dim": D, "chunks": C, "selected": 2051,
             "layers": args.layers, "n_cells": case.n_cells,
         },
-        "achieved_gbs": step_bytes / (ms_per_step * 1e-3) / 1e9,
-        "algorithmic_bytes_per_step": step_bytes,
-        "step_ms_events_median": float(np.median(step_ms)),
+        # every step of the timed region from HIP events on the launch stream
+        "step_ms": stats(step_ms),
+        "value_at_median_step": work / (float(np.median(step_ms)) * 1e-3),
+        "achieved_gbs": achieved,
+        "effective_gbs": step_bytes / (ms_per_step * 1e-3) / 1e9,
+        "per_token_bytes_per_step": step_bytes,
         "kernels": {
-            "qsa_attn": {"avg_us": attn_avg_s * 1e6, "bytes_per_launch": a_bytes, "gbs": attn_gbs},
-            "qsa_merge": {"avg_us": merge_avg_s * 1e6, "bytes_per_launch": m_bytes,
-                          "gbs": m_bytes / merge_avg_s / 1e9},
+            "qsa_attn": {"us": stats(attn_us), "min_bytes_per_launch": a_min, "per_token_bytes_per_launch": a_bytes,
+                         "effective_gbs": a_bytes / attn_avg_s / 1e9},
+            "qsa_merge": {"us": stats(merge_us), "bytes_per_launch": m_bytes,
+                          "gbs": m_bytes / merge_avg_s / 1e9, "frac": m_bytes / merge_avg_s / 1e9 / HBM_PEAK_GBS},
         },
+        # achieved: the fewest HBM bytes one launch can move (each selected cell
+        # once, ids, q, chunk records) over the launch's average time; traffic:
+        # the counted L2-to-memory bytes (FETCH_SIZE + WRITE_SIZE, calibrated)
+        # of the same kernel source, or null when the counters predate it
         "roofline": {
             "bound": "hbm",
-            "achieved": attn_gbs,
+            "achieved": achieved,
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
-            "frac": attn_gbs / HBM_PEAK_GBS,
+            "frac": achieved / HBM_PEAK_GBS,
             "traffic": traffic,
+            "algorithmic_bytes_per_launch": a_min,
+            "kernel": "qsa_attn",
+            "avg_us": attn_avg_s * 1e6,
+            "counted_gbs": None if traffic is None else traffic / attn_avg_s / 1e9,
+            "counted_frac": None if traffic is None else traffic / attn_avg_s / 1e9 / HBM_PEAK_GBS,
+            "per_token_gbs": a_bytes / attn_avg_s / 1e9,
         },
     }
+
+    if args.cold_samples > 0:
+        # the caches are scrubbed before each sample by reading a 1 GiB buffer
+        # (four times the Infinity Cache), outside the sample's events
+        print("bench: %d cold-cache samples" % args.cold_samples, file=sys.stderr, flush=True)
+        scrub = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+        cold = []
+        for _ in range(args.cold_samples):
+            float(scrub.sum())
+            e = [[ev() for _ in range(3)] for _ in range(args.layers)]
+            step(e)
+            torch.cuda.synchronize()
+            cold.append(e[0][0].elapsed_time(e[-1][2]))
+        del scrub
+        result["cold_cache"] = {"step_ms": stats(cold),
+                                "value_at_median_step": work / (float(np.median(cold)) * 1e-3),
+                                "note": "each sample follows a read of 1 GiB that evicts L2 and the Infinity Cache"}
 
     if not args.no_fused:
         # attention and merge in one dispatch (no chunk records in memory)
         fout = [torch.empty(T, H, D, dtype=torch.float16, device=dev) for _ in range(args.layers)]
+
+        def fstep():
+            for li, (q, kq, vq, ksc, vsc) in enumerate(layers):
+                qsa.qsa_attn_merge(q, kq, vq, ksc, vsc, ids, case.pos0, scale, fout[li], stream=stream)
+
         for _ in range(2):
-            for li, (q, kq, vq, ksc, vsc) in enumerate(layers):
-                qsa.qsa_attn_merge(q, kq, vq, ksc, vsc, ids, case.pos0, scale, fout[li], stream=stream)
+            fstep()
         torch.cuda.synchronize()
-        fev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
-        for s in range(args.steps):
-            fev[s][0].record(stream)
-            for li, (q, kq, vq, ksc, vsc) in enumerate(layers):
-                qsa.qsa_attn_merge(q, kq, vq, ksc, vsc, ids, case.pos0, scale, fout[li], stream=stream)
-            fev[s][1].record(stream)
+        fev = [[ev(), ev()] for _ in range(args.steps)]
+        for s_ in range(args.steps):
+            fev[s_][0].record(stream)
+            fstep()
+            fev[s_][1].record(stream)
         torch.cuda.synchronize()
-        f_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in fev]))
+        f_ms = [e[0].elapsed_time(e[1]) for e in fev]
         fdiff = float((fout[0].float() - outs[0].float()).abs().max())
         result["fused_path"] = {
             "entry": "qsa_attn_merge",
-            "value": T * H * args.layers / (f_ms * 1e-3),
+            "value": work / (float(np.median(f_ms)) * 1e-3),
             "unit": "query-token*heads/s",
-            "ms_per_step": f_ms,
-            "avg_us_per_launch": f_ms * 1e3 / args.layers,
+            "step_ms": stats(f_ms),
+            "avg_us_per_launch": float(np.mean(f_ms)) * 1e3 / args.layers,
             "max_abs_diff_vs_two_kernel_path": fdiff,
         }
-        del fout
+        # the same with the sigmoid gate and the per-16 sums
+        gate = up(synth.gates(T, H, seed=5))
+        gsum = torch.empty(T, H, D // 16, dtype=torch.float32, device=dev)
+        q0, kq0, vq0, ks0, vs0 = layers[0]
+        for _ in range(2):
+            qsa.qsa_attn_merge_gated(q0, kq0, vq0, ks0, vs0, ids, case.pos0, scale, gate, fout[0], gsum,
+                                     stream=stream)
+        gev = [[ev(), ev()] for _ in range(args.steps)]
+        for s_ in range(args.steps):
+            gev[s_][0].record(stream)
+            qsa.qsa_attn_merge_gated(q0, kq0, vq0, ks0, vs0, ids, case.pos0, scale, gate, fout[0], gsum,
+                                     stream=stream)
+            gev[s_][1].record(stream)
+        torch.cuda.synchronize()
+        result["gated_fused_path"] = {"entry": "qsa_attn_merge_gated (fp32 gates, per-16 sums)",
+                                      "us_per_launch": stats([1e3 * e[0].elapsed_time(e[1]) for e in gev])}
+        del fout, gate, gsum
 
     if not args.no_score:
         sc = synth.score_case(T=T, pos0=case.pos0, Hs=12)
@@ -263,14 +419,16 @@ def main():
         scores = torch.empty(T, sc.row_stride, dtype=torch.float32, device=dev)
         for _ in range(2):
             qsa.qsa_score(sq, sk, sc.pos0, 1.0, float("-inf"), scores, stream=stream)
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         reps = 10
-        e0.record(stream)
-        for _ in range(reps):
+        sev = [[ev(), ev()] for _ in range(reps)]
+        for e in sev:
+            e[0].record(stream)
             qsa.qsa_score(sq, sk, sc.pos0, 1.0, float("-inf"), scores, stream=stream)
-        e1.record(stream)
+            e[1].record(stream)
         torch.cuda.synchronize()
-        us = e0.elapsed_time(e1) * 1e3 / reps
+        s_us = [1e3 * e[0].elapsed_time(e[1]) for e in sev]
+        us = float(np.mean(s_us))
+        e0, e1 = ev(), ev()
         flops = 2.0 * 128 * sum(case.pos0 + t + 1 for t in range(T))   # heads summed before the contraction
         # the kernel runs each fp32 product as three bf16 products (hi*hi + hi*lo + lo*hi)
         # on the bf16 matrix cores: the roofline is theirs, for the products executed
@@ -286,14 +444,19 @@ def main():
         t_mfma = executed / (BF16_MFMA_PEAK_TFLOPS * 1e12)
         t_hbm = score_bytes / (HBM_PEAK_GBS * 1e9)
         result["companion_score"] = {
-            "workload": "qsa_score T=1984 pos0=30000 Hs=12 fp32",
+            "workload": "qsa_score T=1984 pos0=30000 Hs=12",
+            "dtype": "fp32 in/out, bf16x3 products (each fp32 product split into bf16 parts, hi*hi + hi*lo + lo*hi, "
+                     "fp32 accumulation)",
             "avg_us": us,
-            "fp32_equivalent_tflops": flops / (us * 1e-6) / 1e12,
+            "us": stats(s_us),
             "hbm_gbs": score_bytes / (us * 1e-6) / 1e9,
             "roofline": hbm_roof if t_hbm >= t_mfma else mfma_roof,
             "other_roofline": mfma_roof if t_hbm >= t_mfma else hbm_roof,
             "lower_bound_us": {"hbm": t_hbm * 1e6, "bf16_mfma": t_mfma * 1e6},
         }
+        if not args.no_cpu:
+            print("bench: score errors against the oracle", file=sys.stderr, flush=True)
+            result["companion_score"]["errors"] = score_errors(sc, scores.cpu().numpy(), 24, host_cpu()[0])
         # selection producer on those scores: K = 2051 ids per row (the long-context selection size)
         K_sel = 2051
         sel_stride = 64 * ((K_sel + 63) // 64)
@@ -456,8 +619,7 @@ def main():
 
     if not args.no_cpu:
         print("bench: cpu baseline", file=sys.stderr, flush=True)
-        threads = max(1, min(16, len(os.sched_getaffinity(0))))
-        result["cpu_baseline"] = cpu_baseline(case, outs[0].cpu().numpy(), args.cpu_tokens, threads)
+        result["cpu_baseline"] = cpu_baseline(case, outs[0].cpu().numpy(), args.cpu_tokens, args.cpu_single_tokens)
 
     print(json.dumps(result), flush=True)
     return 0

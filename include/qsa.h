@@ -70,7 +70,7 @@ typedef enum {
  * m = -inf and l = +0, and its o is not written.
  *
  * q        fp16 [T][H][D], row-major, 16-byte aligned
- * kq, vq   int8 [n_cells][D], 16-byte aligned rows; n_cells <= 2^25
+ * kq, vq   int8 [n_cells][D], 16-byte aligned rows; pos0 + T <= n_cells <= 2^25
  * ksc, vsc fp16 [n_cells][D/32], finite and positive, 8-byte aligned
  * ids      int32 [T][ids_stride], -1 = poison. Any id outside [0, n_cells) is
  *          treated as poison and never dereferenced. ids_stride must be a
@@ -79,7 +79,9 @@ typedef enum {
  *          once per occurrence.
  *          ids == NULL selects implicit rows: slot j holds cell j when j <= p
  *          (else poison), with C = ceil((pos0 + T) / 64); ids_stride is ignored.
- * pos0     cache position of token 0 (>= 0); T query tokens (>= 0)
+ * pos0     cache position of token 0 (>= 0); T query tokens (>= 0);
+ *          n_cells >= pos0 + T (the cache holds every causal cell of the
+ *          call), else QSA_ERR_ARG
  * H        query heads sharing the one K/V head, 1..16
  * D        head dim; the library implements D == 128 only
  * scale    softmax scale applied to every dot product
@@ -132,6 +134,46 @@ QSA_API qsa_status qsa_attn_merge(const void *q, const int8_t *kq, const int8_t 
  */
 QSA_API qsa_status qsa_merge(const void *part, int32_t n_chunks, int32_t T, int32_t H, int32_t D,
                      void *out, void *stream);
+
+/*
+ * qsa_merge_gated -- qsa_merge with the sigmoid output gate, and optionally
+ * the per-16 sums of the written output.
+ *
+ * Defined by "round 5 track b: cached residual norms and fused mtp
+ * attention", sections "preflight / ownership" (the merge keeps the sigmoid
+ * gate and the per-16 sums), "mtp attention" and "actual verification" (gates
+ * are fp32 inputs; per-16 sums are compared byte for byte). The pages give
+ * neither the gate's shape nor the sums' tree; the readings taken are one
+ * fp32 gate per output element and the exact sum of each block of 16 written
+ * values:
+ *   y     = sum_k w_k o_k[d] / L          (as qsa_merge; +0 for a row with no chunk)
+ *   out   = fp16_rne(y / (1 + exp(-gate[t][h][d])))
+ *   sums16[t][h][b] = fp32_rne(exact sum_{i<16} out[t][h][16b + i])   (if sums16 != NULL)
+ * gate = +inf gives qsa_merge's output, gate = -inf a zero of y's sign, a
+ * NaN gate a NaN output. The sums depend on no summation order.
+ *
+ * gate     fp32 [T][H][D], 16-byte aligned (required)
+ * out      fp16 [T][H][D], 16-byte aligned
+ * sums16   fp32 [T][H][D/16], 4-byte aligned, or NULL
+ * Other arguments and errors are those of qsa_merge; a NULL gate is QSA_ERR_ARG.
+ */
+QSA_API qsa_status qsa_merge_gated(const void *part, int32_t n_chunks, int32_t T, int32_t H, int32_t D,
+                           const float *gate, void *out, float *sums16, void *stream);
+
+/*
+ * qsa_attn_merge_gated -- qsa_attn_merge with the sigmoid output gate and the
+ * optional per-16 sums, applied as in qsa_merge_gated. This is the pages'
+ * fused decode kernel with its gate ("round 5 track b: cached residual norms
+ * and fused mtp attention", sections "preflight / ownership" and "mtp
+ * attention"). Arguments are those of qsa_attn_merge plus
+ *   gate     fp32 [T][H][D], 16-byte aligned (required)
+ *   sums16   fp32 [T][H][D/16], 4-byte aligned, or NULL
+ */
+QSA_API qsa_status qsa_attn_merge_gated(const void *q, const int8_t *kq, const int8_t *vq,
+                                const void *ksc, const void *vsc, int32_t n_cells,
+                                const int32_t *ids, int32_t ids_stride,
+                                int32_t pos0, int32_t T, int32_t H, int32_t D,
+                                float scale, const float *gate, void *out, float *sums16, void *stream);
 
 /*
  * qsa_score -- fp32 q.K scores over causal cells with a dead-key tail.

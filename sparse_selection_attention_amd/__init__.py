@@ -16,7 +16,7 @@ import torch
 
 __all__ = [
     "QsaError", "CHUNK", "GROUP", "HEAD_DIM",
-    "qsa_attn", "qsa_attn_merge", "qsa_merge", "qsa_score", "qsa_quant_append", "qsa_select", "qsa_part_bytes",
+    "qsa_attn", "qsa_attn_merge", "qsa_attn_merge_gated", "qsa_merge", "qsa_merge_gated", "qsa_score", "qsa_quant_append", "qsa_select", "qsa_part_bytes",
     "qsa_part_offsets",
     "qsa_last_error",
     "alloc_part", "part_views", "chunk_count", "lib", "LIB_PATH",
@@ -54,6 +54,10 @@ def lib() -> ctypes.CDLL:
         L.qsa_attn_merge.restype = ctypes.c_int
         L.qsa_merge.argtypes = [P, i32, i32, i32, i32, P, P]
         L.qsa_merge.restype = ctypes.c_int
+        L.qsa_merge_gated.argtypes = [P, i32, i32, i32, i32, P, P, P, P]
+        L.qsa_merge_gated.restype = ctypes.c_int
+        L.qsa_attn_merge_gated.argtypes = [P, P, P, P, P, i32, P, i32, i32, i32, i32, i32, f32, P, P, P, P]
+        L.qsa_attn_merge_gated.restype = ctypes.c_int
         L.qsa_score.argtypes = [P, P, i32, i32, i32, i32, i32, f32, f32, P, i64, P]
         L.qsa_score.restype = ctypes.c_int
         L.qsa_quant_append.argtypes = [P, P, i32, i32, P, P, P, P, i32, i32, P]
@@ -196,6 +200,46 @@ def qsa_merge(part: torch.Tensor, n_chunks: int, out: torch.Tensor, stream=None)
     if part.numel() * part.element_size() < qsa_part_bytes(T, H, D, n_chunks):
         raise ValueError("part is smaller than qsa_part_bytes(T, H, D, C)")
     _raise_on(lib().qsa_merge(_ptr(part), n_chunks, T, H, D, _ptr(out), _stream(stream)))
+
+
+def _check_gate(gate: torch.Tensor, sums16: Optional[torch.Tensor], T: int, H: int, D: int):
+    _need(gate, "gate", torch.float32, 3)
+    if tuple(gate.shape) != (T, H, D):
+        raise ValueError("gate must be [T][H][D]")
+    if sums16 is not None:
+        _need(sums16, "sums16", torch.float32, 3)
+        if tuple(sums16.shape) != (T, H, D // 16):
+            raise ValueError("sums16 must be [T][H][D/16]")
+
+
+def qsa_merge_gated(part: torch.Tensor, n_chunks: int, gate: torch.Tensor, out: torch.Tensor,
+                    sums16: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Max-first merge with the sigmoid gate: out = fp16(sigmoid(gate) * merged),
+    gate fp32 [T][H][D]; optional per-16 sums of out into sums16 (fp32 [T][H][D/16])."""
+    _need(out, "out", torch.float16, 3)
+    T, H, D = out.shape
+    _check_gate(gate, sums16, T, H, D)
+    if part.device.type != "cuda" or not part.is_contiguous():
+        raise ValueError("part must be a contiguous device tensor")
+    if part.numel() * part.element_size() < qsa_part_bytes(T, H, D, n_chunks):
+        raise ValueError("part is smaller than qsa_part_bytes(T, H, D, C)")
+    _raise_on(lib().qsa_merge_gated(_ptr(part), n_chunks, T, H, D, _ptr(gate), _ptr(out), _ptr(sums16),
+                                    _stream(stream)))
+
+
+def qsa_attn_merge_gated(q: torch.Tensor, kq: torch.Tensor, vq: torch.Tensor, ksc: torch.Tensor,
+                         vsc: torch.Tensor, ids: Optional[torch.Tensor], pos0: int, scale: float,
+                         gate: torch.Tensor, out: torch.Tensor, sums16: Optional[torch.Tensor] = None,
+                         stream=None) -> None:
+    """Attention, merge and sigmoid gate in one dispatch (see qsa_merge_gated)."""
+    T, H, D, n_cells, stride = _check_attn_inputs(q, kq, vq, ksc, vsc, ids)
+    _need(out, "out", torch.float16, 3)
+    if tuple(out.shape) != (T, H, D):
+        raise ValueError("out must be [T][H][D]")
+    _check_gate(gate, sums16, T, H, D)
+    _raise_on(lib().qsa_attn_merge_gated(_ptr(q), _ptr(kq), _ptr(vq), _ptr(ksc), _ptr(vsc), n_cells, _ptr(ids),
+                                         stride, pos0, T, H, D, float(scale), _ptr(gate), _ptr(out), _ptr(sums16),
+                                         _stream(stream)))
 
 
 def qsa_score(q: torch.Tensor, k: torch.Tensor, pos0: int, scale: float, dead: float,

@@ -120,6 +120,9 @@ qsa_status check_attn(const char *fn, const void *q, const int8_t *kq, const int
                     ids_stride);
     if ((int64_t)pos0 + T > INT32_MAX)
         return fail(QSA_ERR_ARG, "%s: pos0 + T overflows int32", fn);
+    if ((int64_t)n_cells < (int64_t)pos0 + T)
+        return fail(QSA_ERR_ARG, "%s: n_cells (%d) < pos0 + T (%lld): the cache must hold every causal cell", fn,
+                    n_cells, (long long)pos0 + T);
     if (n_cells > qsa::kMaxCells)
         return fail(QSA_ERR_UNSUPPORTED, "%s: at most %d cached rows (got %d)", fn, qsa::kMaxCells, n_cells);
     if ((int64_t)T * H > INT32_MAX - 64)
@@ -195,54 +198,66 @@ qsa_status qsa_attn(const void *q, const int8_t *kq, const int8_t *vq,
     return launched(qsa::launch_attn(a, static_cast<hipStream_t>(stream)), "qsa_attn");
 }
 
-qsa_status qsa_attn_merge(const void *q, const int8_t *kq, const int8_t *vq,
-                          const void *ksc, const void *vsc, int32_t n_cells,
-                          const int32_t *ids, int32_t ids_stride,
-                          int32_t pos0, int32_t T, int32_t H, int32_t D,
-                          float scale, void *out, void *stream)
+} // extern "C"
+
+namespace {
+
+qsa_status attn_merge_impl(const char *fn, const void *q, const int8_t *kq, const int8_t *vq, const void *ksc,
+                           const void *vsc, int32_t n_cells, const int32_t *ids, int32_t ids_stride, int32_t pos0,
+                           int32_t T, int32_t H, int32_t D, float scale, const float *gate, void *out, float *sums16,
+                           bool gated, void *stream)
 {
     qsa::AttnArgs a;
     bool noop;
-    qsa_status st = check_attn("qsa_attn_merge", q, kq, vq, ksc, vsc, n_cells, ids, ids_stride, pos0, T, H, D,
-                               scale, a, &noop);
+    qsa_status st = check_attn(fn, q, kq, vq, ksc, vsc, n_cells, ids, ids_stride, pos0, T, H, D, scale, a, &noop);
     if (st != QSA_OK)
         return st;
     if (noop)
         return ok();
     if (!out)
-        return fail(QSA_ERR_ARG, "qsa_attn_merge: NULL out");
+        return fail(QSA_ERR_ARG, "%s: NULL out", fn);
     if (!aligned(out, 16))
-        return fail(QSA_ERR_ARG, "qsa_attn_merge: misaligned out (16 B)");
+        return fail(QSA_ERR_ARG, "%s: misaligned out (16 B)", fn);
+    if (gated && !gate)
+        return fail(QSA_ERR_ARG, "%s: NULL gate", fn);
+    if ((gate && !aligned(gate, 16)) || (sums16 && !aligned(sums16, 4)))
+        return fail(QSA_ERR_ARG, "%s: misaligned gate (16 B) or sums16 (4 B)", fn);
     st = check_device();
     if (st != QSA_OK)
         return st;
     a.out = static_cast<_Float16 *>(out);
+    a.gate = gate;
+    a.sums = sums16;
     a.n_blocks = T;
     a.blocks_per_xcd = (T + 7) / 8;
     if (!ids)   // implicit rows: blocks of (token, head) rows share each chunk's cells
-        return launched(qsa::launch_attn_merge_tile(a, static_cast<hipStream_t>(stream)), "qsa_attn_merge");
-    return launched(qsa::launch_attn_merge(a, static_cast<hipStream_t>(stream)), "qsa_attn_merge");
+        return launched(qsa::launch_attn_merge_tile(a, static_cast<hipStream_t>(stream)), fn);
+    return launched(qsa::launch_attn_merge(a, static_cast<hipStream_t>(stream)), fn);
 }
 
-qsa_status qsa_merge(const void *part, int32_t n_chunks, int32_t T, int32_t H, int32_t D,
-                     void *out, void *stream)
+qsa_status merge_impl(const char *fn, const void *part, int32_t n_chunks, int32_t T, int32_t H, int32_t D,
+                      const float *gate, void *out, float *sums16, bool gated, void *stream)
 {
     if (T < 0 || n_chunks < 0)
-        return fail(QSA_ERR_ARG, "qsa_merge: negative T (%d) or n_chunks (%d)", T, n_chunks);
+        return fail(QSA_ERR_ARG, "%s: negative T (%d) or n_chunks (%d)", fn, T, n_chunks);
     if (H < 1)
-        return fail(QSA_ERR_ARG, "qsa_merge: H must be >= 1 (got %d)", H);
+        return fail(QSA_ERR_ARG, "%s: H must be >= 1 (got %d)", fn, H);
     if (H > qsa::kMaxHeads)
-        return fail(QSA_ERR_UNSUPPORTED, "qsa_merge: at most %d heads (got %d)", qsa::kMaxHeads, H);
+        return fail(QSA_ERR_UNSUPPORTED, "%s: at most %d heads (got %d)", fn, qsa::kMaxHeads, H);
     if (D != qsa::kD)
-        return fail(QSA_ERR_UNSUPPORTED, "qsa_merge: head dim %d not implemented (only %d)", D, qsa::kD);
+        return fail(QSA_ERR_UNSUPPORTED, "%s: head dim %d not implemented (only %d)", fn, D, qsa::kD);
     if (T == 0)
         return ok();
     if (!part || !out)
-        return fail(QSA_ERR_ARG, "qsa_merge: NULL part or out");
+        return fail(QSA_ERR_ARG, "%s: NULL part or out", fn);
+    if (gated && !gate)
+        return fail(QSA_ERR_ARG, "%s: NULL gate", fn);
     if (!aligned(part, 256) || !aligned(out, 16))
-        return fail(QSA_ERR_ARG, "qsa_merge: misaligned pointer (part: 256 B; out: 16 B)");
+        return fail(QSA_ERR_ARG, "%s: misaligned pointer (part: 256 B; out: 16 B)", fn);
+    if ((gate && !aligned(gate, 16)) || (sums16 && !aligned(sums16, 4)))
+        return fail(QSA_ERR_ARG, "%s: misaligned gate (16 B) or sums16 (4 B)", fn);
     if (((int64_t)T * H + 3) / 4 > INT32_MAX)
-        return fail(QSA_ERR_ARG, "qsa_merge: T * H too large for one launch");
+        return fail(QSA_ERR_ARG, "%s: T * H too large for one launch", fn);
     qsa_status st = check_device();
     if (st != QSA_OK)
         return st;
@@ -257,7 +272,45 @@ qsa_status qsa_merge(const void *part, int32_t n_chunks, int32_t T, int32_t H, i
     a.T = T;
     a.H = H;
     a.out = static_cast<_Float16 *>(out);
-    return launched(qsa::launch_merge(a, static_cast<hipStream_t>(stream)), "qsa_merge");
+    a.gate = gate;
+    a.sums = sums16;
+    return launched(qsa::launch_merge(a, static_cast<hipStream_t>(stream)), fn);
+}
+
+} // namespace
+
+extern "C" {
+
+qsa_status qsa_attn_merge(const void *q, const int8_t *kq, const int8_t *vq,
+                          const void *ksc, const void *vsc, int32_t n_cells,
+                          const int32_t *ids, int32_t ids_stride,
+                          int32_t pos0, int32_t T, int32_t H, int32_t D,
+                          float scale, void *out, void *stream)
+{
+    return attn_merge_impl("qsa_attn_merge", q, kq, vq, ksc, vsc, n_cells, ids, ids_stride, pos0, T, H, D, scale,
+                           nullptr, out, nullptr, false, stream);
+}
+
+qsa_status qsa_attn_merge_gated(const void *q, const int8_t *kq, const int8_t *vq,
+                                const void *ksc, const void *vsc, int32_t n_cells,
+                                const int32_t *ids, int32_t ids_stride,
+                                int32_t pos0, int32_t T, int32_t H, int32_t D,
+                                float scale, const float *gate, void *out, float *sums16, void *stream)
+{
+    return attn_merge_impl("qsa_attn_merge_gated", q, kq, vq, ksc, vsc, n_cells, ids, ids_stride, pos0, T, H, D,
+                           scale, gate, out, sums16, true, stream);
+}
+
+qsa_status qsa_merge(const void *part, int32_t n_chunks, int32_t T, int32_t H, int32_t D,
+                     void *out, void *stream)
+{
+    return merge_impl("qsa_merge", part, n_chunks, T, H, D, nullptr, out, nullptr, false, stream);
+}
+
+qsa_status qsa_merge_gated(const void *part, int32_t n_chunks, int32_t T, int32_t H, int32_t D,
+                           const float *gate, void *out, float *sums16, void *stream)
+{
+    return merge_impl("qsa_merge_gated", part, n_chunks, T, H, D, gate, out, sums16, true, stream);
 }
 
 qsa_status qsa_score(const float *q, const float *k, int32_t n_cells, int32_t pos0,

@@ -35,10 +35,10 @@
 //     hi*hi + hi*lo + lo*hi, so the products carry about 22 bits:
 //       - vq * vsc has at most 18 significant bits, so V = V_hi + V_lo exactly,
 //         with V_lo formed by one fp16 fma. When a chunk's largest V scale
-//         reaches 2^9 (so vq * vsc could leave fp16 range) its V scales are
-//         first multiplied by a common power of two that brings the largest
-//         into [1, 2), and that exact power of two is taken back out of the
-//         fp32 result; smaller scales are used as they are;
+//         reaches 2^9 (so vq * vsc could leave fp16 range), the codes are
+//         converted as vq * 2^-k (exact, and free: the byte goes under a
+//         smaller fp16 exponent), which brings every |V| below 65024, and 2^k
+//         is taken back out of the fp32 result; the scales are never rounded;
 //       - p = P_hi + P_lo to within 2^-22 relative;
 //     a single fp16 rounding of p and of v would cost up to 2^-12 |v| per
 //     term, which is too coarse when a chunk holds a few cells whose values
@@ -166,13 +166,15 @@ __device__ inline uint64_t issue_chunk(const AttnArgs &a, const WaveLds &L, int3
     return mask;
 }
 
-// Publish the chunk's scales to LDS. V scales get a common power-of-two factor
-// when vq * vsc could leave fp16 range; returns that factor's inverse (1 when
-// no factor was needed) through `down` and whether one was applied.
-__device__ inline bool stage_scales(const WaveLds &L, int lane, uint2 ks, uint2 vs, float &down)
+// Publish the chunk's scales to LDS. When vq * vsc could leave fp16 range (the
+// chunk's largest V scale reaches 2^9), the V codes are converted as
+// vq * 2^-k, k = e - 23 (e the largest biased V-scale exponent, so k <= 7),
+// and the exact factor 2^k must be put back on the result. Returns k (0 when
+// no factor is needed), uniform over the wave.
+__device__ inline int stage_scales(const WaveLds &L, int lane, uint2 ks, uint2 vs)
 {
-    uint32_t ev = max(max((vs.x >> 10) & 31u, (vs.x >> 26) & 31u),
-                      max((vs.y >> 10) & 31u, (vs.y >> 26) & 31u));
+    const uint32_t ev = max(max((vs.x >> 10) & 31u, (vs.x >> 26) & 31u),
+                            max((vs.y >> 10) & 31u, (vs.y >> 26) & 31u));
     uint32_t e = 0;                 // largest biased exponent in the chunk, bit by bit
 #pragma unroll
     for (int bit = 4; bit >= 0; --bit) {
@@ -180,28 +182,19 @@ __device__ inline bool stage_scales(const WaveLds &L, int lane, uint2 ks, uint2 
         if (__ballot(ev >= c) != 0)
             e = c;
     }
-    // |vq| <= 127 and vsc < 2^(e - 14): no overflow below vsc = 2^9
-    const bool renorm = e >= 24;
-    down = 1.0f;
-    uint2 vn = vs;
-    if (renorm) {
-        down = __int_as_float((127 - 15 + (int)e) << 23);           // 2^(e - 15)
-        const float up = __int_as_float((127 + 15 - (int)e) << 23); // 2^(15 - e)
-        _Float16 h0 = (_Float16)(half_bits_to_float(vs.x & 0xffffu) * up);
-        _Float16 h1 = (_Float16)(half_bits_to_float(vs.x >> 16) * up);
-        _Float16 h2 = (_Float16)(half_bits_to_float(vs.y & 0xffffu) * up);
-        _Float16 h3 = (_Float16)(half_bits_to_float(vs.y >> 16) * up);
-        vn.x = (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
-        vn.y = (uint32_t)__builtin_bit_cast(uint16_t, h2) | ((uint32_t)__builtin_bit_cast(uint16_t, h3) << 16);
-    }
     L.ksc[lane] = ks;
-    L.vsc[0 * kChunk + lane] = (uint16_t)(vn.x & 0xffffu);
-    L.vsc[1 * kChunk + lane] = (uint16_t)(vn.x >> 16);
-    L.vsc[2 * kChunk + lane] = (uint16_t)(vn.y & 0xffffu);
-    L.vsc[3 * kChunk + lane] = (uint16_t)(vn.y >> 16);
+    L.vsc[0 * kChunk + lane] = (uint16_t)(vs.x & 0xffffu);
+    L.vsc[1 * kChunk + lane] = (uint16_t)(vs.x >> 16);
+    L.vsc[2 * kChunk + lane] = (uint16_t)(vs.y & 0xffffu);
+    L.vsc[3 * kChunk + lane] = (uint16_t)(vs.y >> 16);
     wave_sync_lds();
-    return renorm;
+    // |vq| <= 127 and vsc < 2^(e - 14): no overflow below vsc = 2^9; above,
+    // |vq * 2^-k * vsc| < 127 * 2^9 = 65024
+    return e >= 24 ? (int)e - 23 : 0;
 }
+
+// 2^k as a float, for 0 <= k <= 7
+__device__ inline float pow2f(int k) { return __int_as_float((127 + k) << 23); }
 
 // Scaled scores of the chunk: S[b][r] is cell 16b + 4j + r, head c16; empty
 // slots get -inf.
@@ -261,10 +254,21 @@ __device__ inline float chunk_probs(const float (&S)[4][4], float ref, float (&P
     return lsum + __shfl_xor(lsum, 32, 64);
 }
 
-// O[tt] += p V over the chunk: O[tt] is heads 4j + r, dim 8*c16 + tt.
+// O[tt] += p V over the chunk: O[tt] is heads 4j + r, dim 8*c16 + tt. The V
+// codes are converted times 2^-k_renorm (see stage_scales); V_hi is
+// the fp16 product with the scale and V_lo its exact residual from one fp16
+// fma (the product has at most 18 significant bits; when it is scaled by 2^-k
+// its lowest bits may fall below the fp16 grid, and V_lo then rounds by at
+// most 2^-25, i.e. 2^(k - 25) <= 2^-18 of the unscaled value).
 __device__ inline void pv_accumulate(const float (&P)[4][4], const uint2 (&vraw)[2][8], const WaveLds &L, int j,
-                                     int c16, floatx4 (&O)[8])
+                                     int c16, int k_renorm, floatx4 (&O)[8])
 {
+    // the two conversion words are wave-uniform; stating that they live in
+    // scalar registers keeps the scheduler from holding more vector values
+    // live in the records kernel (129 VGPRs, three waves per SIMD, without
+    // it; 128 and four with it)
+    I8Scale cv = i8_scale(k_renorm);
+    asm volatile("" : "+s"(cv.xr), "+s"(cv.bias));
 #pragma unroll
     for (int ks2 = 0; ks2 < 2; ++ks2) {
         // A operand: p of slots s = cells 32ks + 16(s/4) + 4j + s%4, as hi + lo
@@ -290,9 +294,9 @@ __device__ inline void pv_accumulate(const float (&P)[4][4], const uint2 (&vraw)
             for (int sp = 0; sp < 4; ++sp) {
                 const uint2 x = vraw[ks2][2 * sp], y = vraw[ks2][2 * sp + 1];
                 const uint32_t xs = tt < 4 ? x.x : x.y, ys = tt < 4 ? y.x : y.y;
-                const half2v vi = __builtin_bit_cast(half2v, cvt2_sel(tt & 3, xs, ys));
+                const half2v vi = __builtin_bit_cast(half2v, cvt2_sel(tt & 3, xs, ys, cv));
                 const half2v hi = vi * sc[sp];                              // round to nearest
-                const half2v lo = __builtin_elementwise_fma(vi, sc[sp], -hi); // exact residual
+                const half2v lo = __builtin_elementwise_fma(vi, sc[sp], -hi); // residual, one rounding
                 vh[sp] = __builtin_bit_cast(uint32_t, hi);
                 vl[sp] = __builtin_bit_cast(uint32_t, lo);
             }
@@ -347,8 +351,7 @@ __global__ __launch_bounds__(64) void attn_kernel(AttnArgs a)
     __builtin_amdgcn_s_waitcnt(0);   // the K tile copy has landed
     wave_sync_lds();
 
-    float down;
-    const bool renorm = stage_scales(L, lane, ks, vs, down);
+    const int kr = stage_scales(L, lane, ks, vs);
     float S[4][4];
     chunk_scores(a.scale, L, qop, mask, j, c16, S);
     const float mx = chunk_max(S);
@@ -358,10 +361,11 @@ __global__ __launch_bounds__(64) void attn_kernel(AttnArgs a)
 #pragma unroll
     for (int tt = 0; tt < 8; ++tt)
         O[tt] = (floatx4){0.f, 0.f, 0.f, 0.f};
-    pv_accumulate(P, vraw, L, j, c16, O);
+    pv_accumulate(P, vraw, L, j, c16, kr, O);
 
     // ---- write the chunk record ----------------------------------------------
-    if (renorm) {                   // take the V scales' power of two back out, exactly
+    if (kr != 0) {                  // take the V codes' power of two back out, exactly
+        const float down = pow2f(kr);
 #pragma unroll
         for (int tt = 0; tt < 8; ++tt)
             O[tt] *= down;
@@ -390,7 +394,12 @@ __global__ __launch_bounds__(64) void attn_kernel(AttnArgs a)
 // M to max(M, m), its probabilities are taken against the new M and the old
 // (L, O) are rescaled by exp(M_old - M_new) -- the combination of chunk records
 // relative to the largest maximum, accumulated as it goes. The waves' (M, L, O)
-// are then combined the same way through LDS and divided once.
+// are then combined the same way through LDS and divided once. The gated
+// entry point then multiplies each value by sigmoid(g) of its fp32 gate before
+// the fp16 rounding and may write the exact per-16 sums of the written values
+// ("round 5 track b: cached residual norms and fused mtp attention", section
+// "preflight / ownership": the fused kernel keeps the sigmoid gate and the
+// per-16 sums).
 
 __global__ __launch_bounds__(64 * kWavesMax) void attn_merge_kernel(AttnArgs a)
 {
@@ -433,8 +442,7 @@ __global__ __launch_bounds__(64 * kWavesMax) void attn_merge_kernel(AttnArgs a)
         id_next = slot_id(a, t, min(k + nw, a.C - 1), lane);   // in flight during this chunk
         if (mask == 0)
             continue;                            // uniform: an empty chunk adds nothing
-        float down;
-        const bool renorm = stage_scales(L, lane, ks, vs, down);
+        const int kr = stage_scales(L, lane, ks, vs);
         half8 qop[4];
         q_operand(a, qrows, j, c16, qop);
         float S[4][4];
@@ -452,14 +460,15 @@ __global__ __launch_bounds__(64 * kWavesMax) void attn_merge_kernel(AttnArgs a)
             for (int tt = 0; tt < 8; ++tt)
                 O[tt][r] *= ar;
         }
-        if (renorm) {               // the chunk's V scales carry 2^(15 - e): put it back on p
+        if (kr != 0) {              // the chunk's V codes carry 2^-k: put 2^k on p
+            const float down = pow2f(kr);
 #pragma unroll
             for (int b = 0; b < 4; ++b)
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
                     P[b][r] *= down;
         }
-        pv_accumulate(P, vraw, L, j, c16, O);
+        pv_accumulate(P, vraw, L, j, c16, kr, O);
         wave_sync_lds();                         // the tile is rewritten by the next chunk
     }
 
@@ -480,11 +489,13 @@ __global__ __launch_bounds__(64 * kWavesMax) void attn_merge_kernel(AttnArgs a)
     }
     __syncthreads();
     for (int idx = threadIdx.x; idx < a.H * (kD / 4); idx += blockDim.x) {
+        // H * 32 items: the four lanes of one 16-dim block (d4 = 4b .. 4b+3)
+        // are consecutive threads of one wave and run the loop together
         const int h = idx / (kD / 4), d4 = idx - h * (kD / 4);
         float M = -INFINITY;
         for (int v = 0; v < nw; ++v)
             M = fmaxf(M, ((const float *)wave_lds(lds, v).ksc)[h]);
-        uint2 res = make_uint2(0u, 0u);          // +0 when no slot of the row was valid
+        float4 y = make_float4(0.f, 0.f, 0.f, 0.f);   // +0 when no slot of the row was valid
         if (M != -INFINITY) {
             float Ls = 0.0f;
             float4 Os = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -501,12 +512,23 @@ __global__ __launch_bounds__(64 * kWavesMax) void attn_merge_kernel(AttnArgs a)
                 Os.z = fmaf(wv, ov.z, Os.z);
                 Os.w = fmaf(wv, ov.w, Os.w);
             }
-            const _Float16 r0 = (_Float16)(Os.x / Ls), r1 = (_Float16)(Os.y / Ls);
-            const _Float16 r2 = (_Float16)(Os.z / Ls), r3 = (_Float16)(Os.w / Ls);
-            res.x = (uint32_t)__builtin_bit_cast(uint16_t, r0) | ((uint32_t)__builtin_bit_cast(uint16_t, r1) << 16);
-            res.y = (uint32_t)__builtin_bit_cast(uint16_t, r2) | ((uint32_t)__builtin_bit_cast(uint16_t, r3) << 16);
+            y = make_float4(Os.x / Ls, Os.y / Ls, Os.z / Ls, Os.w / Ls);
         }
-        *(uint2 *)(a.out + ((int64_t)t * a.H + h) * kD + 4 * d4) = res;
+        const int64_t orow = ((int64_t)t * a.H + h) * kD + 4 * d4;
+        if (a.gate) {               // uniform: the gated entry point
+            const float4 g = *(const float4 *)(a.gate + orow);
+            y.x *= sigmoid_gate(g.x);
+            y.y *= sigmoid_gate(g.y);
+            y.z *= sigmoid_gate(g.z);
+            y.w *= sigmoid_gate(g.w);
+        }
+        const uint2 res = pack_half4(y.x, y.y, y.z, y.w);
+        *(uint2 *)(a.out + orow) = res;
+        if (a.sums) {               // uniform
+            const double sb = xor_sum(xor_sum(half4_sum(res), 1), 2);
+            if ((d4 & 3) == 0)
+                a.sums[((int64_t)t * a.H + h) * (kD / 16) + (d4 >> 2)] = (float)sb;
+        }
     }
 }
 

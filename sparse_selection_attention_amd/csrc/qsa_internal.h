@@ -28,6 +28,8 @@ struct AttnArgs {
     float *m;                 // [T][C][H]
     float *l;                 // [T][C][H]
     _Float16 *out;            // [T][H][D]      merged output (qsa_attn_merge)
+    const float *gate;        // [T][H][D] fp32 sigmoid-gate inputs, or nullptr (ungated)
+    float *sums;              // [T][H][D/16] per-16 sums of out, or nullptr
     int32_t n_blocks;         // workgroups that carry work: C x T one-wave records, T fused
     int32_t blocks_per_xcd;   // workgroups each XCD walks through
 };
@@ -36,6 +38,8 @@ struct MergeArgs {
     const float *o, *m, *l;
     int32_t C, T, H;
     _Float16 *out;            // [T][H][D]
+    const float *gate;        // [T][H][D] fp32 sigmoid-gate inputs, or nullptr (ungated)
+    float *sums;              // [T][H][D/16] per-16 sums of out, or nullptr
 };
 
 struct ScoreArgs {

@@ -18,10 +18,24 @@
 // no branches: records of empty chunks (or past the end) are still addressed,
 // but their products are discarded by a select, so a stale o never reaches the
 // sums.
+//
+// The gated form (qsa_merge_gated) multiplies each merged value by sigmoid(g)
+// of its own fp32 gate before the fp16 rounding, and can also write the exact
+// sum of every block of 16 written values rounded once to fp32 ("round 5
+// track b: cached residual norms and fused mtp attention", sections
+// "preflight / ownership" and "actual verification": the sigmoid gate, fp32
+// gates and the per-16 sums). A lane holds four consecutive dims, so two xor
+// exchanges in binary64 give each block's sum exactly.
 #include "qsa_internal.h"
+#include "qsa_device.h"
 
 namespace qsa {
 namespace {
+
+using dev::pack_half4;
+using dev::half4_sum;
+using dev::sigmoid_gate;
+using dev::xor_sum;
 
 typedef float f4v __attribute__((ext_vector_type(4)));
 
@@ -50,7 +64,7 @@ __global__ __launch_bounds__(64 * kWaves) void merge_kernel(MergeArgs a)
     for (int s = 16; s >= 1; s >>= 1)
         M = fmaxf(M, __shfl_xor(M, s, 64));
 
-    uint2 res = make_uint2(0u, 0u);
+    float4 y = make_float4(0.f, 0.f, 0.f, 0.f);  // +0 when no chunk of the row had a valid slot
     if (M != -INFINITY) {
         float L = 0.0f;
         float4 O = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -76,13 +90,24 @@ __global__ __launch_bounds__(64 * kWaves) void merge_kernel(MergeArgs a)
                 O.w = use ? fmaf(wk, ov[u].w, O.w) : O.w;
             }
         }
-        const _Float16 r0 = (_Float16)(O.x / L), r1 = (_Float16)(O.y / L);
-        const _Float16 r2 = (_Float16)(O.z / L), r3 = (_Float16)(O.w / L);
-        res.x = (uint32_t)__builtin_bit_cast(uint16_t, r0) | ((uint32_t)__builtin_bit_cast(uint16_t, r1) << 16);
-        res.y = (uint32_t)__builtin_bit_cast(uint16_t, r2) | ((uint32_t)__builtin_bit_cast(uint16_t, r3) << 16);
+        y = make_float4(O.x / L, O.y / L, O.z / L, O.w / L);
     }
+    const int64_t orow = ((int64_t)t * a.H + h) * kD + 4 * l32;
+    if (a.gate) {                   // uniform: the gated entry point
+        const float4 g = live ? *(const float4 *)(a.gate + orow) : make_float4(0.f, 0.f, 0.f, 0.f);
+        y.x *= sigmoid_gate(g.x);
+        y.y *= sigmoid_gate(g.y);
+        y.z *= sigmoid_gate(g.z);
+        y.w *= sigmoid_gate(g.w);
+    }
+    const uint2 res = pack_half4(y.x, y.y, y.z, y.w);
     if (live)
-        *(uint2 *)(a.out + ((int64_t)t * a.H + h) * kD + 4 * l32) = res;
+        *(uint2 *)(a.out + orow) = res;
+    if (a.sums) {                   // uniform; every lane takes part in the exchanges
+        const double s = xor_sum(xor_sum(half4_sum(res), 1), 2);   // dims 16b .. 16b+15, b = l32 / 4
+        if (live && (l32 & 3) == 0)
+            a.sums[((int64_t)t * a.H + h) * (kD / 16) + (l32 >> 2)] = (float)s;
+    }
 }
 
 } // namespace

@@ -38,9 +38,13 @@
 //     tiles, walking every third chunk of the same rows; their states are
 //     combined through LDS at the end (the same max-first rule), so the
 //     longest row block walks a third as many chunks in sequence.
-// The V scales of a chunk whose largest scale reaches 2^9 are multiplied by a
-// common power of two first (vq * vsc could leave fp16 range), taken back out
-// exactly on p. Workgroups start with the heaviest row blocks (the last
+// The gated entry point multiplies each fused output by sigmoid(g) of its fp32
+// gate before the fp16 rounding and may write the exact per-16 sums of the
+// written values ("round 5 track b: cached residual norms and fused mtp
+// attention", section "preflight / ownership").
+// In a chunk whose largest V scale reaches 2^9 (vq * vsc could leave fp16
+// range) the V codes are converted as vq * 2^-k, exactly and at no cost, and
+// 2^k is taken back out exactly on p; the scales are never rounded. Workgroups start with the heaviest row blocks (the last
 // tokens, with the most chunks).
 #include "qsa_internal.h"
 #include "qsa_device.h"
@@ -162,13 +166,13 @@ __device__ inline void stage_tiles(uint8_t *lds, int tid, const Raw &R, uint32_t
         v[s] = ok ? R.v[s] : make_uint2(0u, 0u);
         sb[s] = ok ? R.vs[s] : 0u;
     }
-    half2v sc[2] = {__builtin_bit_cast(half2v, sb[0] | (sb[1] << 16)),
-                    __builtin_bit_cast(half2v, sb[2] | (sb[3] << 16))};
-    if (e >= 24) {              // |vq| <= 127: no overflow below a scale of 2^9
-        const _Float16 up = (_Float16)__int_as_float((127 + 15 - (int)e) << 23);   // 2^(15 - e)
-        sc[0] = sc[0] * up;
-        sc[1] = sc[1] * up;
-    }
+    const half2v sc[2] = {__builtin_bit_cast(half2v, sb[0] | (sb[1] << 16)),
+                          __builtin_bit_cast(half2v, sb[2] | (sb[3] << 16))};
+    // |vq| <= 127: no overflow below a scale of 2^9; above it the codes are
+    // converted as vq * 2^-k, k = e - 23 <= 7 (exact), so |V| < 65024, and p
+    // carries 2^k. V_lo is the residual of the fp16 product from one fp16
+    // fma: exact, or (with the 2^-k) rounded by at most 2^-25 of the scaled value
+    const I8Scale cv = i8_scale(e >= 24 ? (int)e - 23 : 0);
 #pragma unroll
     for (int dd = 0; dd < 8; ++dd) {
         uint32_t vh[2], vl[2];
@@ -176,9 +180,9 @@ __device__ inline void stage_tiles(uint8_t *lds, int tid, const Raw &R, uint32_t
         for (int sp = 0; sp < 2; ++sp) {
             const uint2 x = v[2 * sp], y = v[2 * sp + 1];
             const uint32_t xs = dd < 4 ? x.x : x.y, ys = dd < 4 ? y.x : y.y;
-            const half2v vi = __builtin_bit_cast(half2v, cvt2_sel(dd & 3, xs, ys));
+            const half2v vi = __builtin_bit_cast(half2v, cvt2_sel(dd & 3, xs, ys, cv));
             const half2v hi = vi * sc[sp];                                   // round to nearest
-            const half2v lo = __builtin_elementwise_fma(vi, sc[sp], -hi);    // exact residual
+            const half2v lo = __builtin_elementwise_fma(vi, sc[sp], -hi);    // residual, one rounding
             vh[sp] = __builtin_bit_cast(uint32_t, hi);
             vl[sp] = __builtin_bit_cast(uint32_t, lo);
         }
@@ -328,8 +332,8 @@ __global__ __launch_bounds__(kTileThreads * G) void attn_tile_kernel(AttnArgs a,
             for (int n = 0; n < 8; ++n)
                 O[n] = zero;
         }
-        if (e >= 24) {                          // V carries 2^(15 - e): put 2^(e - 15) on p
-            const float down = __int_as_float((127 - 15 + (int)e) << 23);
+        if (e >= 24) {                          // V carries 2^-(e - 23): put 2^(e - 23) on p
+            const float down = __int_as_float((127 - 23 + (int)e) << 23);
 #pragma unroll
             for (int b = 0; b < 4; ++b)
 #pragma unroll
@@ -410,16 +414,30 @@ __global__ __launch_bounds__(kTileThreads * G) void attn_tile_kernel(AttnArgs a,
         }
     }
     if constexpr (kFused) {
-        if (row_ok && gi == 0) {
-            _Float16 *out = a.out + (int64_t)row * kD + 4 * j;
+        if (gi == 0) {                          // uniform per wave
+            // O[n][r] is dim 16n + 4j + r: block n of 16 dims sits in the four
+            // lanes c16, c16 + 16, c16 + 32, c16 + 48 (the same row)
+            const int64_t obase = (int64_t)(row_ok ? row : 0) * kD + 4 * j;
 #pragma unroll
             for (int n = 0; n < 8; ++n) {
-                half2v lo2 = {(_Float16)0.0f, (_Float16)0.0f}, hi2 = lo2;   // a row with no valid cell gives +0
-                if (Lrun > 0.0f) {
-                    lo2 = (half2v){(_Float16)(O[n][0] / Lrun), (_Float16)(O[n][1] / Lrun)};
-                    hi2 = (half2v){(_Float16)(O[n][2] / Lrun), (_Float16)(O[n][3] / Lrun)};
+                float4 y = make_float4(0.f, 0.f, 0.f, 0.f);   // a row with no valid cell gives +0
+                if (Lrun > 0.0f)
+                    y = make_float4(O[n][0] / Lrun, O[n][1] / Lrun, O[n][2] / Lrun, O[n][3] / Lrun);
+                if (a.gate && row_ok) {         // the gated entry point
+                    const float4 g = *(const float4 *)(a.gate + obase + 16 * n);
+                    y.x *= sigmoid_gate(g.x);
+                    y.y *= sigmoid_gate(g.y);
+                    y.z *= sigmoid_gate(g.z);
+                    y.w *= sigmoid_gate(g.w);
                 }
-                *(uint2 *)(out + 16 * n) = make_uint2(__builtin_bit_cast(uint32_t, lo2), __builtin_bit_cast(uint32_t, hi2));
+                const uint2 res = pack_half4(y.x, y.y, y.z, y.w);
+                if (row_ok)
+                    *(uint2 *)(a.out + obase + 16 * n) = res;
+                if (a.sums) {                   // uniform; every lane takes part in the exchanges
+                    const double sb = xor_sum(xor_sum(half4_sum(res), 16), 32);
+                    if (row_ok && j == 0)
+                        a.sums[(int64_t)row * (kD / 16) + n] = (float)sb;
+                }
             }
         }
     } else {

@@ -60,6 +60,23 @@ int main(void)
     expect(qsa_merge(FAKE, 3, 4, 12, 96, FAKE, NULL), QSA_ERR_UNSUPPORTED, "merge D = 96");
     expect(qsa_merge(FAKE, 3, 4, 0, 128, FAKE, NULL), QSA_ERR_ARG, "merge H = 0");
 
+    expect(qsa_attn(FAKE, FAKE, FAKE, FAKE, FAKE, 13, FAKE, 64, 10, 4, 12, 128, 0.1f, FAKE, NULL), QSA_ERR_ARG,
+           "attn n_cells < pos0 + T");
+
+    /* gated merge and gated fused attention */
+    expect(qsa_merge_gated(FAKE, 3, 0, 12, 128, FAKE, FAKE, FAKE, NULL), QSA_OK, "merge_gated T = 0");
+    expect(qsa_merge_gated(FAKE, 3, 4, 12, 128, NULL, FAKE, FAKE, NULL), QSA_ERR_ARG, "merge_gated NULL gate");
+    expect(qsa_merge_gated(FAKE, 3, 4, 12, 128, AT(8), FAKE, FAKE, NULL), QSA_ERR_ARG,
+           "merge_gated misaligned gate");
+    expect(qsa_merge_gated(FAKE, 3, 4, 12, 128, FAKE, FAKE, AT(2), NULL), QSA_ERR_ARG,
+           "merge_gated misaligned sums");
+    expect(qsa_attn_merge_gated(FAKE, FAKE, FAKE, FAKE, FAKE, 100, FAKE, 64, 10, 0, 12, 128, 0.1f, FAKE, FAKE,
+                                NULL, NULL), QSA_OK, "attn_merge_gated T = 0");
+    expect(qsa_attn_merge_gated(FAKE, FAKE, FAKE, FAKE, FAKE, 100, FAKE, 64, 10, 4, 12, 128, 0.1f, NULL, FAKE,
+                                NULL, NULL), QSA_ERR_ARG, "attn_merge_gated NULL gate");
+    expect(qsa_attn_merge_gated(FAKE, FAKE, FAKE, FAKE, FAKE, 13, FAKE, 64, 10, 4, 12, 128, 0.1f, FAKE, FAKE,
+                                NULL, NULL), QSA_ERR_ARG, "attn_merge_gated n_cells < pos0 + T");
+
     /* score */
     expect(qsa_score(FAKE, FAKE, 100, 10, 0, 12, 128, 1.0f, -1.0f, FAKE, 100, NULL), QSA_OK, "score T = 0");
     expect(qsa_score(FAKE, FAKE, 100, 10, 4, 12, 128, 1.0f, -1.0f, FAKE, 13, NULL), QSA_ERR_ARG,

@@ -25,6 +25,7 @@ def test_library_loads_and_exports_every_declared_symbol():
     L = qsa.lib()
     names = declared_symbols()
     assert {"qsa_attn", "qsa_attn_merge", "qsa_merge", "qsa_score", "qsa_quant_append", "qsa_select",
+            "qsa_merge_gated", "qsa_attn_merge_gated",
             "qsa_part_bytes", "qsa_part_offsets", "qsa_last_error"} <= names
     for n in names:
         assert hasattr(L, n), n
@@ -274,3 +275,81 @@ def test_select_rejects_bad_arguments_on_host(kw, status):
 
 def test_select_zero_rows_is_a_no_op():
     assert select(T=0, scores=None, ids=None) == qsa.QSA_OK
+
+
+# ---------------------------------------------------------------------------
+# the cache must hold every causal cell of the call: n_cells >= pos0 + T
+
+
+@pytest.mark.parametrize("fn", ["attn", "attn_merge", "attn_merge_gated"])
+def test_attention_rejects_a_cache_shorter_than_the_causal_range(fn):
+    call = {"attn": attn, "attn_merge": attn_merge, "attn_merge_gated": attn_merge_gated}[fn]
+    assert call(n_cells=13, pos0=10, T=4) == qsa.QSA_ERR_ARG
+    assert "n_cells" in qsa.qsa_last_error()
+    assert call(n_cells=13, pos0=10, T=4, ids=None) == qsa.QSA_ERR_ARG      # implicit rows too
+    assert call(n_cells=0, pos0=0, T=1) == qsa.QSA_ERR_ARG
+    # exactly pos0 + T cells passes the host checks (the next check needs a device)
+    assert call(n_cells=14, pos0=10, T=4) != qsa.QSA_ERR_ARG
+
+
+# ---------------------------------------------------------------------------
+# gated entry points
+
+
+def attn_merge_gated(**kw):
+    a = dict(q=FAKE, kq=FAKE, vq=FAKE, ksc=FAKE, vsc=FAKE, n_cells=100, ids=FAKE, ids_stride=64,
+             pos0=10, T=4, H=12, D=128, scale=0.1, gate=FAKE, out=FAKE, sums=None)
+    a.update(kw)
+    P = ctypes.c_void_p
+    return qsa.lib().qsa_attn_merge_gated(P(a["q"]), P(a["kq"]), P(a["vq"]), P(a["ksc"]), P(a["vsc"]),
+                                          a["n_cells"], P(a["ids"]), a["ids_stride"], a["pos0"], a["T"], a["H"],
+                                          a["D"], a["scale"], P(a["gate"]), P(a["out"]), P(a["sums"]), P(None))
+
+
+def merge_gated(**kw):
+    a = dict(part=FAKE, C=3, T=2, H=12, D=128, gate=FAKE, out=FAKE, sums=FAKE)
+    a.update(kw)
+    P = ctypes.c_void_p
+    return qsa.lib().qsa_merge_gated(P(a["part"]), a["C"], a["T"], a["H"], a["D"], P(a["gate"]), P(a["out"]),
+                                     P(a["sums"]), P(None))
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(gate=None), qsa.QSA_ERR_ARG),
+    (dict(gate=FAKE + 8), qsa.QSA_ERR_ARG),
+    (dict(sums=FAKE + 2), qsa.QSA_ERR_ARG),
+    (dict(out=None), qsa.QSA_ERR_ARG),
+    (dict(out=FAKE + 8), qsa.QSA_ERR_ARG),
+    (dict(H=17), qsa.QSA_ERR_UNSUPPORTED),
+    (dict(D=64), qsa.QSA_ERR_UNSUPPORTED),
+    (dict(T=-1), qsa.QSA_ERR_ARG),
+    (dict(ids_stride=32), qsa.QSA_ERR_ARG),
+])
+def test_attn_merge_gated_rejects_bad_arguments_on_host(kw, status):
+    assert attn_merge_gated(**kw) == status
+    assert qsa.qsa_last_error().startswith("qsa_attn_merge_gated")
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(gate=None), qsa.QSA_ERR_ARG),
+    (dict(gate=FAKE + 4), qsa.QSA_ERR_ARG),
+    (dict(sums=FAKE + 1), qsa.QSA_ERR_ARG),
+    (dict(part=None), qsa.QSA_ERR_ARG),
+    (dict(part=FAKE + 64), qsa.QSA_ERR_ARG),
+    (dict(out=FAKE + 2), qsa.QSA_ERR_ARG),
+    (dict(C=-1), qsa.QSA_ERR_ARG),
+    (dict(H=0), qsa.QSA_ERR_ARG),
+    (dict(H=17), qsa.QSA_ERR_UNSUPPORTED),
+    (dict(D=96), qsa.QSA_ERR_UNSUPPORTED),
+])
+def test_merge_gated_rejects_bad_arguments_on_host(kw, status):
+    assert merge_gated(**kw) == status
+    assert qsa.qsa_last_error().startswith("qsa_merge_gated")
+
+
+def test_gated_zero_tokens_is_a_no_op():
+    assert merge_gated(T=0, part=None, gate=None, out=None, sums=None) == qsa.QSA_OK
+    assert attn_merge_gated(T=0, q=None, gate=None, out=None) == qsa.QSA_OK
+    # sums16 is optional: a NULL one passes the host checks
+    assert merge_gated(sums=None) != qsa.QSA_ERR_ARG
+    assert attn_merge_gated(sums=None) != qsa.QSA_ERR_ARG

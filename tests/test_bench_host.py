@@ -59,3 +59,38 @@ def test_traffic_is_read_only_for_the_source_it_was_taken_on(tmp_path):
     src.write_text("kernel v2\n")
     assert bench.read_traffic(str(prof), [str(src)]) is None
     assert bench.read_traffic(str(tmp_path / "missing.md"), [str(src)]) is None
+
+
+def test_minimum_bytes_take_each_selected_cell_once():
+    """The roofline's bytes per launch: every distinct selected cell's K and V
+    rows and scales once, every id slot, q, and the records; at the long-context
+    workload the evenly spaced selections of neighbouring tokens overlap, so the
+    distinct cells are far fewer than 1984 x 2051."""
+    T, H, D, C, n_cells = 3, 2, 128, 2, 100
+    ids = np.full((T, 64 * C), -1, dtype=np.int32)
+    ids[0, :10] = np.arange(10)
+    ids[1, :10] = np.arange(10)                      # the same cells again
+    ids[1, 70] = 50
+    ids[2, 3] = n_cells + 7                          # not a cell
+    rec = lambda k: H * (8 * C + 4 * D * k)
+    assert bench.attn_min_bytes(ids, n_cells, T, H, D, C) == 11 * 272 + T * (256 * C + 2 * H * D) + rec(1) + rec(2) + rec(0)
+    case = synth.long_ctx(layers=1)
+    a_min = bench.attn_min_bytes(case.ids, case.n_cells, case.T, case.H, case.D, case.n_chunks)
+    a, _ = bench.attn_bytes(case.ids, case.n_cells, case.T, case.H, case.D, case.n_chunks)
+    uniq = np.unique(case.ids[case.ids >= 0]).size
+    assert uniq < case.n_cells and a_min == a - (1984 * 2051 - uniq) * 272
+    # 8.5 MB of distinct K/V rows: the chunk records (408 MB) dominate
+    assert 430e6 < a_min < 450e6
+
+
+def test_host_cpu_share(monkeypatch):
+    monkeypatch.setenv("OMP_NUM_THREADS", "3")
+    threads, visible, model = bench.host_cpu()
+    assert threads == min(3, visible) and visible == len(os.sched_getaffinity(0)) and model
+    monkeypatch.delenv("OMP_NUM_THREADS")
+    assert bench.host_cpu()[0] == len(os.sched_getaffinity(0))
+
+
+def test_stats():
+    s = bench.stats([3.0, 1.0, 2.0, 10.0])
+    assert s == {"n": 4, "median": 2.5, "min": 1.0, "max": 10.0, "mean": 4.0}

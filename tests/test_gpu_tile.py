@@ -64,42 +64,38 @@ def test_uniform_probe_is_exact():
         assert np.all(np.abs(g - mean) <= np.abs(mean) * (2.0 ** -11 + 2.0 ** -20) + 2.0 ** -25), t
 
 
-def test_cells_past_the_cache_are_not_selected():
-    # n_cells below pos0 + T: cells at or past n_cells count for no row
+def test_cache_shorter_than_the_causal_range_is_refused():
+    """n_cells below pos0 + T is QSA_ERR_ARG for implicit rows, on both paths,
+    and nothing is written."""
     T, pos0, H, n_cells = 90, 60, 12, 100
     L = _case(T, pos0, H, n_cells=n_cells, seed=8)
-    scale = synth.SCALE_1_SQRT_128
-    out, o, m, l, C = run_attn(L, None, pos0, scale, implicit=True)
-    fout = run_fused(L, None, pos0, scale, implicit=True)
-    refs = oracle_tokens(L, None, pos0, scale, list(range(T)))
-    for t, r in refs.items():
-        check_out(out[t], r["out64"], "past-cache t=%d" % t)
-        check_out(fout[t], r["out64"], "past-cache fused t=%d" % t)
-
-
-def test_empty_cache_gives_zero_output():
-    # n_cells = 0 (buffers of one row, none of it a cell): every record empty, output +0
-    import ctypes
-    T, H = 10, 12
-    L = _case(T, 0, H, n_cells=1)
-    dev = torch.device("cuda:0")
-    up = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+    d = torch.device("cuda:0")
+    up = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(d)
     q, kq, vq, ksc, vsc = up(L.q), up(L.kq), up(L.vq), up(L.ksc), up(L.vsc)
-    C = (T + 63) // 64
-    part = torch.full((qsa.qsa_part_bytes(T, H, 128, C),), 0x5A, dtype=torch.uint8, device=dev)
-    out = torch.full((T, H, 128), float("nan"), dtype=torch.float16, device=dev)
-    fout = torch.full((T, H, 128), float("nan"), dtype=torch.float16, device=dev)
-    P = ctypes.c_void_p
-    ptr = lambda x: P(x.data_ptr())
-    st = P(torch.cuda.current_stream().cuda_stream)
-    args = (ptr(q), ptr(kq), ptr(vq), ptr(ksc), ptr(vsc), 0, P(None), 0, 0, T, H, 128, 0.1)
-    assert qsa.lib().qsa_attn(*args, ptr(part), st) == 0
-    assert qsa.lib().qsa_attn_merge(*args, ptr(fout), st) == 0
-    qsa.qsa_merge(part, C, out)
+    C = qsa.chunk_count(None, pos0, T)
+    part = torch.full((qsa.qsa_part_bytes(T, H, 128, C),), 0x5A, dtype=torch.uint8, device=d)
+    out = torch.full((T, H, 128), float("nan"), dtype=torch.float16, device=d)
+    for call in (lambda: qsa.qsa_attn(q, kq, vq, ksc, vsc, None, pos0, 0.1, part),
+                 lambda: qsa.qsa_attn_merge(q, kq, vq, ksc, vsc, None, pos0, 0.1, out)):
+        with pytest.raises(qsa.QsaError) as e:
+            call()
+        assert e.value.status == qsa.QSA_ERR_ARG and "n_cells" in str(e.value)
     torch.cuda.synchronize()
-    o, m, l = qsa.part_views(part, T, H, 128, C)
-    assert torch.all(m == -float("inf")) and torch.all(l.view(torch.int32) == 0)
-    assert torch.all(out.view(torch.int16) == 0) and torch.all(fout.view(torch.int16) == 0)
+    assert torch.all(part == 0x5A) and torch.all(torch.isnan(out))
+
+
+def test_one_cell_cache_and_first_tokens():
+    # the smallest cache a call can take (n_cells = pos0 + T = 1), and the
+    # first tokens of a prompt, whose rows hold one and two cells
+    L = _case(1, 0, 12, seed=4)
+    out, o, m, l, C = run_attn(L, None, 0, 0.1, implicit=True)
+    fout = run_fused(L, None, 0, 0.1, implicit=True)
+    v = L.vq[0].astype(np.float64) * np.repeat(L.vsc[0].astype(np.float64), 32)
+    ref = v.astype(np.float16)                   # one cell: the output is its V row, rounded once
+    for h in range(12):
+        assert np.array_equal(out[0, h].view(np.uint16), ref.view(np.uint16))
+        assert np.array_equal(fout[0, h].view(np.uint16), ref.view(np.uint16))
+    assert np.all(l[0, 0] == 1.0)
 
 
 def test_large_and_tiny_scales():
