@@ -251,6 +251,33 @@ QSA_API qsa_status qsa_quant_append(const float *k, const float *v, int32_t n_ro
 QSA_API qsa_status qsa_select(const float *scores, int64_t row_stride, int32_t pos0, int32_t T, int32_t K,
                       int32_t *ids, int32_t ids_stride, void *stream);
 
+/*
+ * qsa_split_merge_static -- qsa_attn followed by qsa_merge, with the chunk
+ * records kept in a workspace the library holds instead of one the caller
+ * passes.
+ *
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the call
+ * allocates nothing. The records go to a static device array of
+ * QSA_STATIC_PART_BYTES that every GPU the library runs on holds until the
+ * process ends. The result is that of qsa_attn + qsa_merge on the same
+ * arguments (the same kernels run), written to out (fp16 [T][H][D], 16-byte
+ * aligned); the other arguments are those of qsa_attn.
+ *
+ * Limit: qsa_part_bytes(T, H, D, C) <= QSA_STATIC_PART_BYTES (about 32,000
+ * records of head dim 128: e.g. 64 tokens of 33 chunks at 12 heads, or any
+ * decode window), else QSA_ERR_ARG with the sizes in qsa_last_error.
+ * All calls on one GPU share that GPU's array: calls that overlap on one GPU
+ * (from two streams or two host threads without ordering between them) race,
+ * and their outputs are undefined. Calls ordered on one stream do not.
+ */
+#define QSA_STATIC_PART_BYTES (16u << 20)
+QSA_API qsa_status qsa_split_merge_static(const void *q, const int8_t *kq, const int8_t *vq,
+                                  const void *ksc, const void *vsc, int32_t n_cells,
+                                  const int32_t *ids, int32_t ids_stride,
+                                  int32_t pos0, int32_t T, int32_t H, int32_t D,
+                                  float scale, void *out, void *stream);
+
 /* Bytes of the `part` workspace for T tokens, H heads, head dim D, n_chunks chunks. */
 QSA_API size_t qsa_part_bytes(int32_t T, int32_t H, int32_t D, int32_t n_chunks);
 

@@ -16,7 +16,7 @@ import torch
 
 __all__ = [
     "QsaError", "CHUNK", "GROUP", "HEAD_DIM",
-    "qsa_attn", "qsa_attn_merge", "qsa_attn_merge_gated", "qsa_merge", "qsa_merge_gated", "qsa_score", "qsa_quant_append", "qsa_select", "qsa_part_bytes",
+    "qsa_attn", "qsa_attn_merge", "qsa_attn_merge_gated", "qsa_merge", "qsa_merge_gated", "qsa_split_merge_static", "qsa_score", "qsa_quant_append", "qsa_select", "qsa_part_bytes",
     "qsa_part_offsets",
     "qsa_last_error",
     "alloc_part", "part_views", "chunk_count", "lib", "LIB_PATH",
@@ -58,6 +58,8 @@ def lib() -> ctypes.CDLL:
         L.qsa_merge_gated.restype = ctypes.c_int
         L.qsa_attn_merge_gated.argtypes = [P, P, P, P, P, i32, P, i32, i32, i32, i32, i32, f32, P, P, P, P]
         L.qsa_attn_merge_gated.restype = ctypes.c_int
+        L.qsa_split_merge_static.argtypes = [P, P, P, P, P, i32, P, i32, i32, i32, i32, i32, f32, P, P]
+        L.qsa_split_merge_static.restype = ctypes.c_int
         L.qsa_score.argtypes = [P, P, i32, i32, i32, i32, i32, f32, f32, P, i64, P]
         L.qsa_score.restype = ctypes.c_int
         L.qsa_quant_append.argtypes = [P, P, i32, i32, P, P, P, P, i32, i32, P]
@@ -169,6 +171,22 @@ def qsa_attn_merge(q: torch.Tensor, kq: torch.Tensor, vq: torch.Tensor, ksc: tor
         raise ValueError("out must be [T][H][D]")
     _raise_on(lib().qsa_attn_merge(_ptr(q), _ptr(kq), _ptr(vq), _ptr(ksc), _ptr(vsc), n_cells, _ptr(ids), stride,
                                    pos0, T, H, D, float(scale), _ptr(out), _stream(stream)))
+
+
+STATIC_PART_BYTES = 16 << 20
+
+
+def qsa_split_merge_static(q: torch.Tensor, kq: torch.Tensor, vq: torch.Tensor, ksc: torch.Tensor,
+                           vsc: torch.Tensor, ids: Optional[torch.Tensor], pos0: int, scale: float,
+                           out: torch.Tensor, stream=None) -> None:
+    """qsa_attn then qsa_merge with the chunk records in the library's static
+    workspace (no allocation; at most STATIC_PART_BYTES of records)."""
+    T, H, D, n_cells, stride = _check_attn_inputs(q, kq, vq, ksc, vsc, ids)
+    _need(out, "out", torch.float16, 3)
+    if tuple(out.shape) != (T, H, D):
+        raise ValueError("out must be [T][H][D]")
+    _raise_on(lib().qsa_split_merge_static(_ptr(q), _ptr(kq), _ptr(vq), _ptr(ksc), _ptr(vsc), n_cells, _ptr(ids),
+                                           stride, pos0, T, H, D, float(scale), _ptr(out), _stream(stream)))
 
 
 def qsa_attn(q: torch.Tensor, kq: torch.Tensor, vq: torch.Tensor, ksc: torch.Tensor, vsc: torch.Tensor,

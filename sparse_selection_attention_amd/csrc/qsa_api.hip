@@ -11,6 +11,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 namespace {
 
@@ -426,6 +427,109 @@ qsa_status qsa_select(const float *scores, int64_t row_stride, int32_t pos0, int
     a.ids = ids;
     a.ids_stride = ids_stride;
     return launched(qsa::launch_select(a, static_cast<hipStream_t>(stream)), "qsa_select");
+}
+
+} // extern "C"
+
+// ---- split path through a static workspace (qsa_split_merge_static) ---------
+//
+// For callers that cannot allocate: the chunk records go to `scratch`, a
+// file-scope device array of QSA_STATIC_PART_BYTES that every GPU holds from
+// the library's load until the process ends. Host code never passes the
+// array's name to a kernel or a copy (on the host it is only a stand-in): the
+// first call on a device, with that device current, asks the runtime for the
+// array's device address on that device and keeps it. Nothing in it needs to
+// start at zero: qsa_attn writes every record's (m, l) and every non-empty
+// record's o, and the merge reads o only for non-empty records.
+
+namespace qsa {
+__device__ __align__(256) uint8_t scratch[QSA_STATIC_PART_BYTES];
+} // namespace qsa
+
+namespace {
+
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];    // device address of `scratch` on each device, once known
+
+qsa_status static_workspace(void **ptr)
+{
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return fail(QSA_ERR_DEVICE, "hipGetDevice: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(QSA_ERR_UNSUPPORTED, "device index %d out of range", dev);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(qsa::scratch));
+        if (e != hipSuccess || !p)
+            return fail(QSA_ERR_DEVICE, "hipGetSymbolAddress(scratch) on device %d: %s", dev,
+                        hipGetErrorString(e));
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return QSA_OK;
+}
+
+} // namespace
+
+extern "C" {
+
+qsa_status qsa_split_merge_static(const void *q, const int8_t *kq, const int8_t *vq,
+                                  const void *ksc, const void *vsc, int32_t n_cells,
+                                  const int32_t *ids, int32_t ids_stride,
+                                  int32_t pos0, int32_t T, int32_t H, int32_t D,
+                                  float scale, void *out, void *stream)
+{
+    const char *fn = "qsa_split_merge_static";
+    qsa::AttnArgs a;
+    bool noop;
+    qsa_status st = check_attn(fn, q, kq, vq, ksc, vsc, n_cells, ids, ids_stride, pos0, T, H, D, scale, a, &noop);
+    if (st != QSA_OK)
+        return st;
+    if (noop)
+        return ok();
+    if (!out)
+        return fail(QSA_ERR_ARG, "%s: NULL out", fn);
+    if (!aligned(out, 16))
+        return fail(QSA_ERR_ARG, "%s: misaligned out (16 B)", fn);
+    size_t o_off, m_off, l_off, total;
+    qsa::part_layout(T, H, D, a.C, &o_off, &m_off, &l_off, &total);
+    if (total > QSA_STATIC_PART_BYTES)
+        return fail(QSA_ERR_ARG, "%s: the chunk records of this call need %zu bytes, more than the static "
+                    "workspace's %zu (T * chunks * H <= about %zu records of head dim %d)", fn, total,
+                    (size_t)QSA_STATIC_PART_BYTES, (size_t)QSA_STATIC_PART_BYTES / (4 * (qsa::kD + 2)), qsa::kD);
+    const int64_t n_blocks = (int64_t)a.C * T;
+    const int64_t per_xcd = (n_blocks + 7) / 8;
+    st = check_device();
+    if (st != QSA_OK)
+        return st;
+    void *ws = nullptr;
+    st = static_workspace(&ws);
+    if (st != QSA_OK)
+        return st;
+    char *pb = static_cast<char *>(ws);
+    a.o = reinterpret_cast<float *>(pb + o_off);
+    a.m = reinterpret_cast<float *>(pb + m_off);
+    a.l = reinterpret_cast<float *>(pb + l_off);
+    a.n_blocks = (int32_t)n_blocks;
+    a.blocks_per_xcd = (int32_t)per_xcd;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    st = launched(ids ? qsa::launch_attn(a, s) : qsa::launch_attn_tile(a, s), fn);
+    if (st != QSA_OK)
+        return st;
+    qsa::MergeArgs mg;
+    mg.o = a.o;
+    mg.m = a.m;
+    mg.l = a.l;
+    mg.C = a.C;
+    mg.T = T;
+    mg.H = H;
+    mg.out = static_cast<_Float16 *>(out);
+    mg.gate = nullptr;
+    mg.sums = nullptr;
+    return launched(qsa::launch_merge(mg, s), fn);
 }
 
 } // extern "C"

@@ -353,3 +353,37 @@ def test_gated_zero_tokens_is_a_no_op():
     # sums16 is optional: a NULL one passes the host checks
     assert merge_gated(sums=None) != qsa.QSA_ERR_ARG
     assert attn_merge_gated(sums=None) != qsa.QSA_ERR_ARG
+
+
+# ---------------------------------------------------------------------------
+# the split path through the library's static workspace
+
+
+def split_static(**kw):
+    a = dict(q=FAKE, kq=FAKE, vq=FAKE, ksc=FAKE, vsc=FAKE, n_cells=40000, ids=FAKE, ids_stride=2112,
+             pos0=30000, T=64, H=12, D=128, scale=0.1, out=FAKE)
+    a.update(kw)
+    P = ctypes.c_void_p
+    return qsa.lib().qsa_split_merge_static(P(a["q"]), P(a["kq"]), P(a["vq"]), P(a["ksc"]), P(a["vsc"]),
+                                            a["n_cells"], P(a["ids"]), a["ids_stride"], a["pos0"], a["T"], a["H"],
+                                            a["D"], a["scale"], P(a["out"]), P(None))
+
+
+def test_split_static_limit_and_host_checks():
+    # 64 tokens of 33 chunks at 12 heads fit the 16 MiB workspace; 90 do not
+    assert qsa.qsa_part_bytes(64, 12, 128, 33) <= qsa.STATIC_PART_BYTES < qsa.qsa_part_bytes(90, 12, 128, 33)
+    assert split_static(T=90) == qsa.QSA_ERR_ARG
+    assert "static workspace" in qsa.qsa_last_error()
+    assert split_static(T=64) != qsa.QSA_ERR_ARG           # fits: the next check needs a device
+    assert split_static(T=0, q=None, out=None) == qsa.QSA_OK
+    assert split_static(out=None) == qsa.QSA_ERR_ARG
+    assert split_static(out=FAKE + 8) == qsa.QSA_ERR_ARG
+    assert split_static(n_cells=100) == qsa.QSA_ERR_ARG    # n_cells < pos0 + T
+    assert split_static(H=17) == qsa.QSA_ERR_UNSUPPORTED
+    assert split_static(ids=None, pos0=0, n_cells=6000, T=6000, H=12) == qsa.QSA_ERR_ARG   # implicit rows too large
+
+
+def test_static_workspace_size_matches_the_header():
+    text = open(os.path.join(ROOT, "include", "qsa.h")).read()
+    m = re.search(r"#define QSA_STATIC_PART_BYTES \((\d+)u << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == qsa.STATIC_PART_BYTES
