@@ -63,7 +63,8 @@ constexpr int kWavesMax = 8;               // over few chunks (one wave each), o
 constexpr int kKTileBytes = kChunk * kD;                 // 8 KB of K rows per wave
 constexpr int kWaveBytes = kKTileBytes + kChunk * 8      // K tile, K scales (fp16 x 4)
                            + kChunk * 8 + kChunk * 4;    // V scales (group-major), cell ids
-constexpr int attn_lds_bytes(int nw, int H) { return nw * kWaveBytes + H * kD * 2; }
+// (gated calls only) then the token's fp32 gate rows
+constexpr int attn_lds_bytes(int nw, int H, bool gated) { return nw * kWaveBytes + H * kD * 2 + (gated ? H * kD * 4 : 0); }
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -103,6 +104,20 @@ __device__ inline void copy_q_rows(const AttnArgs &a, uint8_t *qrows, int t, int
             const int lg = phys ^ (h & 15);
             const _Float16 *src = a.q + ((int64_t)t * a.H + h) * kD + 8 * lg;
             __builtin_amdgcn_global_load_lds((const void *)src, (lds_void *)(qrows + 16 * g0), 16, 0, 0);
+        }
+    }
+}
+
+// The token's fp32 gate rows (H x 512 B, in memory order) into LDS, 1 KB per
+// load, shared by waves 0..nw-1. Issued once the q rows have landed, so they
+// complete under the first chunk's gathers instead of at the end.
+__device__ inline void copy_gate_rows(const AttnArgs &a, uint8_t *grows, int t, int w, int nw, int lane)
+{
+    for (int g0 = 64 * w; g0 < 32 * a.H; g0 += 64 * nw) {
+        const int gi = g0 + lane;                // destination granule: head gi / 32, dims 4 (gi % 32) ..
+        if (gi < 32 * a.H) {
+            const float *src = a.gate + (int64_t)t * a.H * kD + 4 * gi;
+            __builtin_amdgcn_global_load_lds((const void *)src, (lds_void *)(grows + 16 * g0), 16, 0, 0);
         }
     }
 }
@@ -415,9 +430,12 @@ __global__ __launch_bounds__(64 * kWavesMax) void attn_merge_kernel(AttnArgs a)
 
     const WaveLds L = wave_lds(lds, w);
     uint8_t *qrows = lds + nw * kWaveBytes;
+    uint8_t *grows = qrows + a.H * kD * 2;       // gated calls only
     copy_q_rows(a, qrows, t, w, nw, lane0);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
+    if (a.gate)                                  // uniform
+        copy_gate_rows(a, grows, t, w, nw, lane0);
 
     float Mrun = -INFINITY, Lrun = 0.0f;         // head c16
     floatx4 O[8];                                // heads 4j + r, dim 8*c16 + tt
@@ -473,6 +491,7 @@ __global__ __launch_bounds__(64 * kWavesMax) void attn_merge_kernel(AttnArgs a)
     }
 
     // ---- combine the waves: (M, L) and O through LDS, then divide once ---
+    __builtin_amdgcn_s_waitcnt(0);               // this wave's gate copies have landed
     const int j = lane0 >> 4, c16 = lane0 & 15;
     float *sM = (float *)L.ksc;                  // 16 floats
     float *sL = sM + 16;                         // 16 floats
@@ -516,7 +535,7 @@ __global__ __launch_bounds__(64 * kWavesMax) void attn_merge_kernel(AttnArgs a)
         }
         const int64_t orow = ((int64_t)t * a.H + h) * kD + 4 * d4;
         if (a.gate) {               // uniform: the gated entry point
-            const float4 g = *(const float4 *)(a.gate + orow);
+            const float4 g = *(const float4 *)(grows + 16 * (h * (kD / 4) + d4));
             y.x *= sigmoid_gate(g.x);
             y.y *= sigmoid_gate(g.y);
             y.z *= sigmoid_gate(g.z);
@@ -549,7 +568,7 @@ hipError_t launch_attn_merge(const AttnArgs &a, hipStream_t stream)
     // serial walk over the chunks (2051 cells at T = 1: 33.8 -> 26.4 us)
     const int nw = a.C <= kWavesMax ? a.C : (a.T <= 64 ? kWavesMax : kWaves);
     dim3 grid(8 * a.blocks_per_xcd), block(64 * nw);
-    hipLaunchKernelGGL(attn_merge_kernel, grid, block, attn_lds_bytes(nw, a.H), stream, a);
+    hipLaunchKernelGGL(attn_merge_kernel, grid, block, attn_lds_bytes(nw, a.H, a.gate != nullptr), stream, a);
     return hipGetLastError();
 }
 

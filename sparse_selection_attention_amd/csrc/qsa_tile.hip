@@ -11,29 +11,41 @@
 // of one contraction: row r is token r / H, head r % H, which is also q's and
 // the output's memory order.
 //
-// Design on CDNA4. A workgroup of four waves owns 64 consecutive rows, 16 per
+// Design on CDNA4. A group of four waves owns 64 consecutive rows, 16 per
 // wave, and walks the chunks up to its last token's causal edge:
-//   * staging, once per chunk for all four waves: half the threads read the
-//     chunk's 64 K rows and write them to LDS as fp16 (exact), the other half
-//     read the V rows and write V transposed (dims x cells) as fp16 high and
-//     low parts with V_hi + V_lo = vq * vsc exactly, cells permuted so that
-//     each PV operand read is one 16-byte load; both tiles are XOR-swizzled in
-//     16-byte granules for conflict-free operand reads;
+//   * reads: the next chunk's K and V rows are read into registers while the
+//     current chunk is contracted; each K read instruction covers whole
+//     128-byte cache rows (eight lanes of 16 bytes per row), each V read gives
+//     a lane 8 dims of one of four consecutive cells (the layout the
+//     transposed tile is written in), and the K and V scales of the chunk's
+//     64 cells are one contiguous 512-byte run each;
+//   * staging, once per chunk for all four waves: K to LDS as fp16 (exact),
+//     [cell][dim]; V transposed, [dim][position], as its int8 codes in fp16
+//     (exact), cells permuted so that each PV operand read is one 16-byte
+//     load; both tiles are XOR-swizzled in 16-byte granules for conflict-free
+//     operand reads. The V scales go to LDS per scale group, each group times
+//     its own power of two 2^kg, chosen from the chunk's largest scale of the
+//     group so that p * vsc * 2^kg stays below 2^15;
 //   * QK: v_mfma_f32_16x16x32_f16 with A = 16 cells x 32 dims of one scale
 //     group and B = the wave's 16 q rows, one fp32 partial per scale group,
 //     weighted by the cell's group scale; a lane then holds 16 of its row's
-//     64 scores, so the row max and sum are lane folds plus two exchanges;
+//     64 scores, so the row max and sum are lane folds plus two exchanges.
+//     Scores are kept in log2 units (the softmax scale is applied times
+//     log2(e)), so p = exp2(S - max) needs no multiply;
 //   * causality is a per-row mask: cell c counts for row r iff
 //     c <= pos0 + r / H (and c < n_cells);
-//   * PV: O^T = V^T P^T on the same MFMA, A = V^T from LDS, B = p straight
-//     from the score registers, both split into fp16 high and low parts and
-//     contracted as hi*hi + hi*lo + lo*hi (about 22 bits per product);
+//   * PV: O^T = V^T P^T on the same MFMA. Each MFMA's 16 output dims lie in
+//     one scale group, so the group's V scales fold into p: B = p * vsc * 2^kg
+//     as fp16 high and low parts (high: the fp16 product; low: its residual
+//     from one fp16 fma plus the low part of p times the scale), and A = the
+//     exact V codes. Two MFMAs per tile carry about 22 bits of each product,
+//     and 2^-kg comes back out exactly;
 //   * chunk records (qsa_attn): one (m, l, o) per row and chunk, rows past
 //     their causal edge writing the empty record (-inf, 0); the chunks of a
 //     row block are split over workgroups of at most 8 chunks each, so the
-//     long rows of late tokens do not serialise; fused
-//     (qsa_attn_merge): a running max, denominator and output per row,
-//     rescaled as each chunk's max arrives, divided once at the end. A fused
+//     long rows of late tokens do not serialise; fused (qsa_attn_merge): a
+//     running max, denominator and output per row, rescaled as each chunk's
+//     max (or a group's power of two) moves, divided once at the end. A fused
 //     workgroup holds three such groups of four waves, each with its own LDS
 //     tiles, walking every third chunk of the same rows; their states are
 //     combined through LDS at the end (the same max-first rule), so the
@@ -42,10 +54,8 @@
 // gate before the fp16 rounding and may write the exact per-16 sums of the
 // written values ("round 5 track b: cached residual norms and fused mtp
 // attention", section "preflight / ownership").
-// In a chunk whose largest V scale reaches 2^9 (vq * vsc could leave fp16
-// range) the V codes are converted as vq * 2^-k, exactly and at no cost, and
-// 2^k is taken back out exactly on p; the scales are never rounded. Workgroups start with the heaviest row blocks (the last
-// tokens, with the most chunks).
+// Workgroups start with the heaviest row blocks (the last tokens, with the most
+// chunks).
 #include "qsa_internal.h"
 #include "qsa_device.h"
 
@@ -57,139 +67,201 @@ using namespace dev;
 constexpr int kTileRows = 64;                  // (token, head) rows per workgroup
 constexpr int kTileThreads = 256;
 
-// LDS layout
+// LDS layout of one group
 constexpr int kLK = 0;                         // K fp16 [64 cells][128 dims], 256-byte rows
-constexpr int kLVh = kLK + kChunk * kD * 2;    // V^T hi fp16 [128 dims][64 positions], 128-byte rows
-constexpr int kLVl = kLVh + kD * kChunk * 2;   // V^T lo
-constexpr int kLKs = kLVl + kD * kChunk * 2;   // K scales fp16 [64 cells][4]
-constexpr int kLE = kLKs + kChunk * 8;         // int[4]: largest V-scale exponent seen by each wave
-constexpr int kTileLds = kLE + 16;
+constexpr int kLV = kLK + kChunk * kD * 2;     // V^T codes fp16 [128 dims][64 positions], 128-byte rows
+constexpr int kLKs = kLV + kD * kChunk * 2;    // K scales fp16 [64 cells][4]
+constexpr int kVsRow = 144;                    // one group's 64 V scales (128 B) plus a 16-byte pad
+constexpr int kLVs = kLKs + kChunk * 8;        // V scales times 2^kg, fp16 [4 groups][kVsRow bytes]
+constexpr int kLE = kLVs + 4 * kVsRow;         // int[4 waves][4 groups]: largest V-scale exponents
+constexpr int kGroupState = 4 * 64 * 36 * 4;   // end-of-walk (M, L, O) of the group's 256 lanes
+constexpr int kTileLds = (kLE + 64 > kGroupState) ? kLE + 64 : kGroupState;
 constexpr int kSplit = 8;                      // chunks per workgroup in the chunk-record kernel
 constexpr int kFusedGroups = 3;                // groups of four waves per fused workgroup
-static_assert(kTileLds % 16 == 0 && 4 * 64 * 36 * 4 <= kTileLds, "group state must fit a group's tiles");
+static_assert(kTileLds % 16 == 0, "group regions stay 16-byte aligned");
 
 // K tile: cell c's logical granule gi (dims 8gi .. 8gi+7) at gi ^ (c & 15)
 __device__ inline int tk_offset(int c, int gi) { return kLK + c * 256 + ((gi ^ (c & 15)) << 4); }
-// V^T tiles: dim d's logical granule gp (positions 8gp .. 8gp+7) at gp ^ ((d >> 1) & 7)
-__device__ inline int tv_offset(int base, int d, int gp) { return base + d * 128 + ((gp ^ ((d >> 1) & 7)) << 4); }
+// V^T tile: dim d's logical granule gp (positions 8gp .. 8gp+7) at gp ^ ((d >> 1) & 7)
+__device__ inline int tv_offset(int d, int gp) { return kLV + d * 128 + ((gp ^ ((d >> 1) & 7)) << 4); }
 
-// Position pos = 32ks + 8j + s of a 64-cell chunk holds cell 32ks + 16(s/4) + 4j + s%4:
-// the cells whose scores lane group j holds, in PV operand slot order.
-__device__ inline int pos_cell(int ks, int j, int s) { return 32 * ks + 16 * (s >> 2) + 4 * j + (s & 3); }
+// Position 32ks + 8j + s of a 64-cell chunk holds cell 32ks + 16(s/4) + 4j + s%4:
+// the cells whose scores lane group j holds, in PV operand slot order. The
+// inverse: cell c sits at position 32(c/32) + 8((c%16)/4) + 4((c%32)/16) + c%4.
+__device__ inline int cell_pos(int c)
+{
+    return 32 * (c >> 5) + 8 * ((c >> 2) & 3) + 4 * ((c >> 4) & 1) + (c & 3);
+}
 
-// Every thread stages 32 bytes of K and 32 bytes of V per chunk:
-//   K: cell kc = tid / 4, dims 32 kg .. +31 (kg = tid % 4, one scale group);
-//   V: dims 8 db .. +7 (db = tid / 16) of positions 4 pq .. 4 pq + 3
-//      (pq = tid % 16), which are four consecutive cells.
-struct Raw {
-    uint4 k[2];        // K: 32 bytes of cell kc
-    uint32_t ks;       // K: that cell's scale of group kg (fp16 bits)
-    uint2 v[4];        // V: 8 dims of 4 cells
-    uint32_t vs[4];    // V: the 4 cells' scales of dim group db / 4 (fp16 bits)
-    uint32_t ok;       // bit 0: cell kc exists; bits 1..4: the V cells exist
-};
-
+// What each thread (wave w, lane L) reads of a chunk, into registers:
+//   K: cells 16w + 8i + L/8 (i = 0, 1), dims 16(L%8) .. +15 -- eight lanes
+//      per 128-byte row, eight rows per instruction;
+//   V: dims 8db .. +7 (db = tid / 16) of the four consecutive cells at
+//      positions 4pq .. 4pq + 3 (pq = tid % 16), in the layout the transposed
+//      tile is written in: sixteen lanes then store one dim's sixteen 8-byte
+//      pieces into distinct banks;
+//   scales: cell 16w + L/4, group L%4, of K and of V -- the chunk's scales
+//      are one contiguous 512-byte run.
 __device__ inline int v_cell0(int pq) { return 32 * (pq >> 3) + 16 * (pq & 1) + 4 * ((pq >> 1) & 3); }
 
-// Issue the chunk's global reads into registers. Every read is unconditional
-// (cells past the cache read the last cached row) so that the reads stay in
-// flight; the cells that do not exist are zeroed when the tiles are staged.
-// Byte offsets fit 32 bits: n_cells * 128 < 2^32.
+struct Raw {
+    uint4 k[2];        // K: 16 bytes of each of two cells
+    uint2 v[4];        // V: 8 dims of 4 consecutive cells
+    uint32_t ks, vs;   // the K and V scale of one (cell, group), fp16 bits
+    uint32_t ok;       // bits 0..1: the K cells exist; 2: the scales' cell; 3..6: the V cells
+};
+
+// Issue the chunk's global reads. Every read is unconditional (cells past the
+// cache read the last cached row) so that the reads stay in flight; the cells
+// that do not exist are zeroed when the tiles are staged. Byte offsets fit 32
+// bits: n_cells * 128 < 2^32.
 __device__ inline void load_raw(const AttnArgs &a, int c0, int tid, Raw &R)
 {
     const int last = a.n_cells - 1;     // >= 0 whenever a chunk is walked
-    const int kc = tid >> 2, kg = tid & 3;
-    const int ck = c0 + kc;
-    uint32_t ok = ck <= last ? 1u : 0u;
-    const uint32_t kcc = (uint32_t)min(ck, last);
-    const uint4 *src = (const uint4 *)(a.kq + (kcc * kD + 32 * kg));
-    R.k[0] = src[0];
-    R.k[1] = src[1];
-    R.ks = a.ksc[kcc * 4 + kg];
+    const int w = tid >> 6, L = tid & 63;
+    uint32_t ok = 0;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int c = c0 + 16 * w + 8 * i + (L >> 3);
+        ok |= (c <= last ? 1u : 0u) << i;
+        const uint32_t cc = (uint32_t)min(c, last);
+        R.k[i] = *(const uint4 *)(a.kq + (cc * kD + 16 * (L & 7)));
+    }
+    const int cs = c0 + 16 * w + (L >> 2);
+    ok |= (cs <= last ? 1u : 0u) << 2;
+    const uint32_t ccs = (uint32_t)min(cs, last);
+    R.ks = a.ksc[ccs * 4 + (L & 3)];
+    R.vs = a.vsc[ccs * 4 + (L & 3)];
     const int db = tid >> 4, pq = tid & 15;
-    const int cv = c0 + v_cell0(pq);
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-        ok |= (cv + s <= last ? 1u : 0u) << (1 + s);
-        const uint32_t vcc = (uint32_t)min(cv + s, last);
-        R.v[s] = *(const uint2 *)(a.vq + (vcc * kD + 8 * db));
-        R.vs[s] = a.vsc[vcc * 4 + (db >> 2)];
+        const int c = c0 + v_cell0(pq) + s;
+        ok |= (c <= last ? 1u : 0u) << (3 + s);
+        const uint32_t cc = (uint32_t)min(c, last);
+        R.v[s] = *(const uint2 *)(a.vq + (cc * kD + 8 * db));
     }
     R.ok = ok;
 }
 
-// Largest biased V-scale exponent over this thread's existing V cells.
-__device__ inline uint32_t vs_exponent(const Raw &R)
+// Largest biased exponent of this thread's V scale over the lanes of the wave
+// that hold the same scale group (lane % 4); 0 for a cell that does not exist.
+__device__ inline int group_max_exponent(const Raw &R)
 {
-    uint32_t e = 0;
-#pragma unroll
-    for (int s = 0; s < 4; ++s)
-        e = max(e, ((R.ok >> (1 + s)) & 1u) ? (R.vs[s] >> 10) & 31u : 0u);
-    return e;
+    int e = ((R.ok >> 2) & 1u) ? (int)((R.vs >> 10) & 31u) : 0;
+    e = max(e, __shfl_xor(e, 4, 64));
+    e = max(e, __shfl_xor(e, 8, 64));
+    e = max(e, __shfl_xor(e, 16, 64));
+    return max(e, __shfl_xor(e, 32, 64));
 }
 
-// The same maximum over the wave, bit by bit with ballots (uniform result).
-__device__ inline uint32_t wave_max_exponent(uint32_t ev)
-{
-    uint32_t e = 0;
-#pragma unroll
-    for (int bit = 4; bit >= 0; --bit) {
-        const uint32_t c = e | (1u << bit);
-        if (__ballot(ev >= c) != 0)
-            e = c;
-    }
-    return e;
-}
+// The power of two that scale group g carries in this chunk: with eg the
+// group's largest biased fp16 exponent, every scale is below 2^(eg - 14), so
+// scale * 2^(29 - eg) < 2^15 and p * scale * 2^kg stays clear of the fp16
+// limit. Scaling up is exact in fp16 (eg = 30 gives kg = -1, which may round
+// scales below 2^-13 by the half of an fp16 subnormal step).
+__device__ inline int group_shift(int eg) { return 29 - eg; }
 
-// Convert the chunk's raw rows into the LDS tiles. `e` is the chunk's largest
-// biased V-scale exponent.
-__device__ inline void stage_tiles(uint8_t *lds, int tid, const Raw &R, uint32_t e)
+// 2^k as a float (|k| < 126)
+__device__ inline float pow2i(int k) { return __int_as_float((127 + k) << 23); }
+
+// Convert the chunk's raw rows into the LDS tiles. kg[g] is scale group g's
+// power of two for this chunk.
+__device__ inline void stage_tiles(uint8_t *lds, int tid, const Raw &R, const int (&kg)[4])
 {
-    // K: 32 dims of cell kc as fp16 (exact), and its group scale
-    const int kc = tid >> 2, kg = tid & 3;
-    const bool okk = (R.ok & 1u) != 0;
+    const int w = tid >> 6, L = tid & 63;
+    // K: 16 dims (granules 2m and 2m + 1, m = L % 8) of each of two cells as
+    // fp16 (exact)
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-        const uint4 kr = okk ? R.k[i] : make_uint4(0u, 0u, 0u, 0u);
-        *(half8 *)(lds + tk_offset(kc, 4 * kg + 2 * i)) = i8x8_to_half8(make_uint2(kr.x, kr.y));
-        *(half8 *)(lds + tk_offset(kc, 4 * kg + 2 * i + 1)) = i8x8_to_half8(make_uint2(kr.z, kr.w));
+        const int c = 16 * w + 8 * i + (L >> 3);
+        const uint4 kr = ((R.ok >> i) & 1u) ? R.k[i] : make_uint4(0u, 0u, 0u, 0u);
+        *(half8 *)(lds + tk_offset(c, 2 * (L & 7))) = i8x8_to_half8(make_uint2(kr.x, kr.y));
+        *(half8 *)(lds + tk_offset(c, 2 * (L & 7) + 1)) = i8x8_to_half8(make_uint2(kr.z, kr.w));
     }
-    *(uint16_t *)(lds + kLKs + kc * 8 + 2 * kg) = okk ? (uint16_t)R.ks : (uint16_t)0;
-
-    // V: dims 8db .. +7 of positions 4pq .. +3 as fp16 hi + lo, transposed
-    const int db = tid >> 4, pq = tid & 15;
+    // the (cell, group) scales: K as read, V times 2^kg at the cell's position
+    const int cs = 16 * w + (L >> 2), g = L & 3;
+    const bool oks = ((R.ok >> 2) & 1u) != 0;
+    *(uint16_t *)(lds + kLKs + cs * 8 + 2 * g) = oks ? (uint16_t)R.ks : (uint16_t)0;
+    const int kgs = g == 0 ? kg[0] : g == 1 ? kg[1] : g == 2 ? kg[2] : kg[3];
+    const _Float16 vsn = (_Float16)(half_bits_to_float(R.vs) * pow2i(kgs));
+    *(_Float16 *)(lds + kLVs + g * kVsRow + 2 * cell_pos(cs)) = oks ? vsn : (_Float16)0.0f;
+    // V: dims 8db .. +7 of positions 4pq .. +3 as fp16 codes (exact), transposed
     uint2 v[4];
-    uint32_t sb[4];
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-        const bool ok = ((R.ok >> (1 + s)) & 1u) != 0;
-        v[s] = ok ? R.v[s] : make_uint2(0u, 0u);
-        sb[s] = ok ? R.vs[s] : 0u;
-    }
-    const half2v sc[2] = {__builtin_bit_cast(half2v, sb[0] | (sb[1] << 16)),
-                          __builtin_bit_cast(half2v, sb[2] | (sb[3] << 16))};
-    // |vq| <= 127: no overflow below a scale of 2^9; above it the codes are
-    // converted as vq * 2^-k, k = e - 23 <= 7 (exact), so |V| < 65024, and p
-    // carries 2^k. V_lo is the residual of the fp16 product from one fp16
-    // fma: exact, or (with the 2^-k) rounded by at most 2^-25 of the scaled value
-    const I8Scale cv = i8_scale(e >= 24 ? (int)e - 23 : 0);
+    for (int s = 0; s < 4; ++s)
+        v[s] = ((R.ok >> (3 + s)) & 1u) ? R.v[s] : make_uint2(0u, 0u);
+    const I8Scale cv = i8_scale(0);
+    const int db = tid >> 4, pq = tid & 15;
+    const int gp = pq >> 1, half = 8 * (pq & 1);
 #pragma unroll
     for (int dd = 0; dd < 8; ++dd) {
-        uint32_t vh[2], vl[2];
-#pragma unroll
-        for (int sp = 0; sp < 2; ++sp) {
-            const uint2 x = v[2 * sp], y = v[2 * sp + 1];
-            const uint32_t xs = dd < 4 ? x.x : x.y, ys = dd < 4 ? y.x : y.y;
-            const half2v vi = __builtin_bit_cast(half2v, cvt2_sel(dd & 3, xs, ys, cv));
-            const half2v hi = vi * sc[sp];                                   // round to nearest
-            const half2v lo = __builtin_elementwise_fma(vi, sc[sp], -hi);    // residual, one rounding
-            vh[sp] = __builtin_bit_cast(uint32_t, hi);
-            vl[sp] = __builtin_bit_cast(uint32_t, lo);
-        }
+        const uint32_t x0 = dd < 4 ? v[0].x : v[0].y, x1 = dd < 4 ? v[1].x : v[1].y;
+        const uint32_t x2 = dd < 4 ? v[2].x : v[2].y, x3 = dd < 4 ? v[3].x : v[3].y;
         const int d = 8 * db + dd;
-        const int half = 8 * (pq & 1);
-        *(uint2 *)(lds + tv_offset(kLVh, d, pq >> 1) + half) = make_uint2(vh[0], vh[1]);
-        *(uint2 *)(lds + tv_offset(kLVl, d, pq >> 1) + half) = make_uint2(vl[0], vl[1]);
+        *(uint2 *)(lds + tv_offset(d, gp) + half) =
+            make_uint2(cvt2_sel(dd & 3, x0, x1, cv), cvt2_sel(dd & 3, x2, x3, cv));
+    }
+}
+
+// Scores of the chunk's 64 cells for this lane's row, in log2 units: the four
+// group partials of QK weighted by the cells' K scales, times kmul (the
+// softmax scale times log2(e)); cells past the row's last valid cell get -inf.
+__device__ inline void qk_scores(const uint8_t *lds, const half8 (&qop)[4], int j, int c16, int c0, int lim,
+                                 float kmul, float (&S)[4][4])
+{
+    const floatx4 zero = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+        floatx4 acc[4];
+        const int ca = 16 * b + c16;            // A operand row: cell ca, dims 32g + 8j .. +7
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+            acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(*(const half8 *)(lds + tk_offset(ca, 4 * g + j)),
+                                                            qop[g], zero, 0, 0, 0);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int cell = 16 * b + 4 * j + r;
+            const uint2 kb = *(const uint2 *)(lds + kLKs + cell * 8);
+            float dot = acc[0][r] * half_bits_to_float(kb.x & 0xffffu);
+            dot = __builtin_fmaf(acc[1][r], half_bits_to_float(kb.x >> 16), dot);
+            dot = __builtin_fmaf(acc[2][r], half_bits_to_float(kb.y & 0xffffu), dot);
+            dot = __builtin_fmaf(acc[3][r], half_bits_to_float(kb.y >> 16), dot);
+            S[b][r] = c0 + cell <= lim ? kmul * dot : -INFINITY;
+        }
+    }
+}
+
+// O[n] += the chunk's V codes weighted by p * vsc * 2^kg: O[n][r] is dim
+// 16n + 4j + r of this lane's row, in units of 2^kg of its scale group n / 2.
+__device__ inline void pv_accumulate(const uint8_t *lds, const float (&P)[4][4], int j, int c16, floatx4 (&O)[8])
+{
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+        // p of positions 32ks + 8j + s (cells 32ks + 16(s/4) + 4j + s%4) as
+        // fp16 high and low parts, p = hi + lo to within 2^-22
+        half8 ph, pl;
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+            const float pv = P[2 * ks + (s >> 2)][s & 3];
+            const _Float16 hi = (_Float16)pv;
+            ph[s] = hi;
+            pl[s] = (_Float16)(pv - (float)hi);
+        }
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            // those positions' scales of group g (times 2^kg): B = p * scale as
+            // the fp16 product, plus its exact residual and the low part of p
+            const half8 sc = *(const half8 *)(lds + kLVs + g * kVsRow + 2 * (32 * ks + 8 * j));
+            const half8 bh = ph * sc;
+            const half8 bl = __builtin_elementwise_fma(pl, sc, __builtin_elementwise_fma(ph, sc, -bh));
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const int n = 2 * g + u;
+                const half8 va = *(const half8 *)(lds + tv_offset(16 * n + c16, 4 * ks + j));
+                O[n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, bh, O[n], 0, 0, 0);
+                O[n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, bl, O[n], 0, 0, 0);
+            }
+        }
     }
 }
 
@@ -228,6 +300,7 @@ __global__ __launch_bounds__(kTileThreads * G) void attn_tile_kernel(AttnArgs a,
     const int t = row_ok ? row / a.H : 0;
     const int h = row_ok ? row - t * a.H : 0;
     const int lim = row_ok ? (int)min((int64_t)a.pos0 + t, (int64_t)a.n_cells - 1) : -1;   // last valid cell
+    const float kmul = a.scale * kLog2e;        // scores in log2 units
 
     half8 qop[4];
 #pragma unroll
@@ -241,6 +314,7 @@ __global__ __launch_bounds__(kTileThreads * G) void attn_tile_kernel(AttnArgs a,
         load_raw(a, (k_lo + gi) * kChunk, tid, R);
 
     float Mrun = -INFINITY, Lrun = 0.0f;
+    int krun[4] = {0, 0, 0, 0};                 // the powers of two O carries per scale group
     floatx4 O[8];
 #pragma unroll
     for (int n = 0; n < 8; ++n)
@@ -255,43 +329,26 @@ __global__ __launch_bounds__(kTileThreads * G) void attn_tile_kernel(AttnArgs a,
         // chunk's reads, which are issued before them
         __builtin_amdgcn_s_waitcnt(0);
         if (act) {
-            const uint32_t ew = wave_max_exponent(vs_exponent(R));
-            if (lane == 0)
-                s_e[w] = (int)ew;
+            const int eg = group_max_exponent(R);
+            if (lane < 4)
+                s_e[4 * w + lane] = eg;         // lane l holds scale group l
         }
         __syncthreads();                        // the previous chunk's tiles are no longer read
-        const uint32_t e = (uint32_t)max(max(s_e[0], s_e[1]), max(s_e[2], s_e[3]));
+        int kg[4];
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+            kg[g] = group_shift(max(max(s_e[g], s_e[4 + g]), max(s_e[8 + g], s_e[12 + g])));
         if (act)
-            stage_tiles(lds, tid, R, e);
+            stage_tiles(lds, tid, R, kg);
         __syncthreads();                        // the chunk's tiles are in place
         if (!act)
             continue;
         if (k + G <= k_end)
             load_raw(a, c0 + G * kChunk, tid, R);   // in flight during this chunk's contractions
 
-        // ---- QK: S[b][r] is cell 16b + 4j + r of this lane's row ----------------
+        // ---- QK: S[b][r] is cell 16b + 4j + r of this lane's row, log2 units ---
         float S[4][4];
-        const floatx4 zero = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int b = 0; b < 4; ++b) {
-            floatx4 acc[4];
-            const int ca = 16 * b + c16;        // A operand row: cell ca, dims 32g + 8j .. +7
-#pragma unroll
-            for (int g = 0; g < 4; ++g)
-                acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(*(const half8 *)(lds + tk_offset(ca, 4 * g + j)),
-                                                                qop[g], zero, 0, 0, 0);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int cell = 16 * b + 4 * j + r;
-                const uint2 kb = *(const uint2 *)(lds + kLKs + cell * 8);
-                float dot = acc[0][r] * half_bits_to_float(kb.x & 0xffffu);
-                dot = __builtin_fmaf(acc[1][r], half_bits_to_float(kb.x >> 16), dot);
-                dot = __builtin_fmaf(acc[2][r], half_bits_to_float(kb.y & 0xffffu), dot);
-                dot = __builtin_fmaf(acc[3][r], half_bits_to_float(kb.y >> 16), dot);
-                const float sv = a.scale * dot;
-                S[b][r] = c0 + cell <= lim ? sv : -INFINITY;
-            }
-        }
+        qk_scores(lds, qop, j, c16, c0, lim, kmul, S);
         float mx = -INFINITY;
 #pragma unroll
         for (int b = 0; b < 4; ++b)
@@ -306,7 +363,7 @@ __global__ __launch_bounds__(kTileThreads * G) void attn_tile_kernel(AttnArgs a,
         if constexpr (kFused) {
             const float Mnew = fmaxf(Mrun, mx);
             ref = Mnew == -INFINITY ? 0.0f : Mnew;
-            alpha = Mnew == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f((Mrun - Mnew) * kLog2e);  // 0 when Mrun = -inf
+            alpha = Mnew == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(Mrun - Mnew);  // 0 when Mrun = -inf
             Mrun = Mnew;
         } else {
             ref = mx == -INFINITY ? 0.0f : mx;
@@ -317,69 +374,56 @@ __global__ __launch_bounds__(kTileThreads * G) void attn_tile_kernel(AttnArgs a,
         for (int b = 0; b < 4; ++b)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                P[b][r] = __builtin_amdgcn_exp2f((S[b][r] - ref) * kLog2e);    // exp(-inf) = 0, exp(0) = 1
+                P[b][r] = __builtin_amdgcn_exp2f(S[b][r] - ref);    // exp2(-inf) = 0, exp2(0) = 1
                 lsum += P[b][r];
             }
         lsum += __shfl_xor(lsum, 16, 64);
         lsum += __shfl_xor(lsum, 32, 64);
         if constexpr (kFused) {
+            // what came before: times alpha, and moved to this chunk's powers of two
             Lrun = fmaf(alpha, Lrun, lsum);
+            const bool same_k = kg[0] == krun[0] && kg[1] == krun[1] && kg[2] == krun[2] && kg[3] == krun[3];
+            if (!same_k || __ballot(alpha != 1.0f) != 0) {   // uniform
 #pragma unroll
-            for (int n = 0; n < 8; ++n)
-                O[n] *= alpha;
+                for (int g = 0; g < 4; ++g) {
+                    const float f = alpha * pow2i(kg[g] - krun[g]);
+                    O[2 * g] *= f;
+                    O[2 * g + 1] *= f;
+                    krun[g] = kg[g];
+                }
+            }
         } else {
 #pragma unroll
             for (int n = 0; n < 8; ++n)
-                O[n] = zero;
-        }
-        if (e >= 24) {                          // V carries 2^-(e - 23): put 2^(e - 23) on p
-            const float down = __int_as_float((127 - 23 + (int)e) << 23);
-#pragma unroll
-            for (int b = 0; b < 4; ++b)
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    P[b][r] *= down;
+                O[n] = (floatx4){0.f, 0.f, 0.f, 0.f};
         }
 
         // ---- PV: O[n][r] is dim 16n + 4j + r of this lane's row -----------------
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            half8 pb_hi, pb_lo;
-#pragma unroll
-            for (int s = 0; s < 8; ++s) {
-                const float pv = P[2 * ks + (s >> 2)][s & 3];
-                const _Float16 hi = (_Float16)pv;
-                pb_hi[s] = hi;
-                pb_lo[s] = (_Float16)(pv - (float)hi);
-            }
-#pragma unroll
-            for (int n = 0; n < 8; ++n) {
-                const int d = 16 * n + c16;     // A operand row: dim d, positions 32ks + 8j .. +7
-                const half8 va_hi = *(const half8 *)(lds + tv_offset(kLVh, d, 4 * ks + j));
-                const half8 va_lo = *(const half8 *)(lds + tv_offset(kLVl, d, 4 * ks + j));
-                O[n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va_hi, pb_hi, O[n], 0, 0, 0);
-                O[n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va_hi, pb_lo, O[n], 0, 0, 0);
-                O[n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va_lo, pb_hi, O[n], 0, 0, 0);
-            }
-        }
+        pv_accumulate(lds, P, j, c16, O);
 
         if constexpr (!kFused) {
             if (row_ok) {
                 const int64_t rec = ((int64_t)t * a.C + k) * a.H + h;
                 if (j == 0) {
-                    a.m[rec] = mx;
+                    a.m[rec] = mx * kLn2;            // back from log2 units; -inf stays -inf
                     a.l[rec] = mx == -INFINITY ? 0.0f : lsum;
                 }
                 if (mx != -INFINITY) {          // an empty record leaves o alone
                     float *o = a.o + rec * kD + 4 * j;
 #pragma unroll
                     for (int n = 0; n < 8; ++n)
-                        *(floatx4 *)(o + 16 * n) = O[n];
+                        *(floatx4 *)(o + 16 * n) = O[n] * pow2i(-kg[n >> 1]);
                 }
             }
         }
     }
 
+    if constexpr (kFused) {
+        // back to plain units: each scale group's power of two comes out exactly
+#pragma unroll
+        for (int n = 0; n < 8; ++n)
+            O[n] *= pow2i(-krun[n >> 1]);
+    }
     if constexpr (kFused && G > 1) {
         // combine the groups: each lane's (M, L, O) has the same row and dims in
         // every group; groups 1.. publish theirs over their own tiles
@@ -401,8 +445,8 @@ __global__ __launch_bounds__(kTileThreads * G) void attn_tile_kernel(AttnArgs a,
                 const float M = fmaxf(Mrun, M2);
                 if (M == -INFINITY)
                     continue;                   // neither has seen a valid cell
-                const float a1 = __builtin_amdgcn_exp2f((Mrun - M) * kLog2e);   // 0 when Mrun = -inf
-                const float a2 = __builtin_amdgcn_exp2f((M2 - M) * kLog2e);
+                const float a1 = __builtin_amdgcn_exp2f(Mrun - M);   // 0 when Mrun = -inf (log2 units)
+                const float a2 = __builtin_amdgcn_exp2f(M2 - M);
                 Lrun = a1 * Lrun + a2 * L2;
 #pragma unroll
                 for (int n = 0; n < 8; ++n) {

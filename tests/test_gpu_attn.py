@@ -77,6 +77,33 @@ def test_long_context_three_layers():
     _print("long", check_attn_case(synth.long_ctx(layers=3), n_sample=12))
 
 
+@pytest.mark.parametrize("name", ["mid", "long"])
+def test_every_token_of_layer0(name):
+    """Every one of the 1984 tokens of layer 0, on the records path (records
+    and merged output) and on the fused path, against the oracle; the
+    three-layer tests above sample layers 1 and 2."""
+    import concurrent.futures as cf
+    from gpu_util import THREADS
+    case = synth.mid(layers=1) if name == "mid" else synth.long_ctx(layers=1)
+    L = case.layers[0]
+    out, o, m, l, C = run_attn(L, case.ids, case.pos0, case.scale)
+    fout = run_fused(L, case.ids, case.pos0, case.scale)
+    toks = list(range(case.T))
+    refs = oracle_tokens(L, case.ids, case.pos0, case.scale, toks)
+
+    def one(t):
+        r = refs[t]
+        e1 = check_out(out[t], r["out64"], "%s records path t=%d" % (name, t))
+        e2 = check_out(fout[t], r["out64"], "%s fused t=%d" % (name, t))
+        check_records(o[t], m[t], l[t], r, chunk_magnitude(L, case.ids, case.pos0, case.scale, t, C), t, name)
+        return max(e1[0], e2[0]), max(e1[1], e2[1])
+
+    with cf.ThreadPoolExecutor(THREADS) as ex:
+        errs = list(ex.map(one, toks))
+    _print("%s layer 0, all %d tokens: worst abs %.3g rel %.3g" % (name, case.T, max(e[0] for e in errs),
+                                                                  max(e[1] for e in errs)))
+
+
 @pytest.mark.parametrize("variant", ["signed_zero", "cancel"])
 def test_long_context_edge_variants(variant):
     case = synth.long_ctx(layers=1, variant=variant)
