@@ -62,6 +62,28 @@ def attn_min_bytes(ids, n_cells, T, H, D, C):
     return uniq * (2 * D + 2 * 2 * (D // 32)) + 4 * 64 * C * T + 2 * H * D * T + int((H * (8 * C + 4 * D * c)).sum())
 
 
+# Address-unit cost of one vector-memory instruction of a 64-lane wave, in CU
+# cycles, by access shape (a microbenchmark of random L2-resident rows on gfx950;
+# the cost follows the distinct rows each group of four lanes touches)
+GATHER_CYCLES = {"16B_lane_8_rows": 21, "8B_lane_4_rows": 21, "8B_lane_16_rows": 66, "8B_lane_64_rows": 85}
+CLOCK_GHZ = 2.4
+
+
+def attn_gather_model(T, c_nonempty, n_cu=256):
+    """Lower bound on qsa_attn's time from its load instructions alone: per
+    non-empty (token, chunk) wave, 8 K-row copies (16 B per lane, 8 full rows),
+    16 V-row loads (8 B per lane, 4 full rows), 2 scale loads (8 B per lane, 64
+    rows), 4 q loads (16 rows per instruction, costed as the 16-row shape) and 1
+    id load (64 consecutive ids, costed as a full-row shape), spread evenly over
+    the CUs. The record stores are not modelled."""
+    g = GATHER_CYCLES
+    per_wave = (8 * g["16B_lane_8_rows"] + 16 * g["8B_lane_4_rows"] + 2 * g["8B_lane_64_rows"]
+                + 4 * g["8B_lane_16_rows"] + 1 * g["16B_lane_8_rows"])
+    waves = int(c_nonempty.sum())
+    return {"cycles_per_wave": per_wave, "waves": waves, "cus": n_cu, "clock_ghz": CLOCK_GHZ,
+            "us": waves / n_cu * per_wave / (CLOCK_GHZ * 1e3)}
+
+
 def merge_bytes(T, H, D, C, c):
     # reads (m, l) of every chunk and o of non-empty chunks, writes fp16 out
     return int((H * 8 * C + H * 4 * D * c + 2 * H * D).sum()) if hasattr(c, "sum") else None
@@ -162,7 +184,8 @@ def cpu_baseline(case, out_gpu, n_tokens, single_tokens):
         "kind": "oracle",
         "sample": "%d evenly spaced tokens of layer 0 of the same workload (fp64 C oracle, %d threads, %.1f s wall)"
                   % (n_tokens, threads, dt),
-        "host": {"cpu_model": model, "logical_cpus_visible": visible, "threads_used": threads,
+        "host": {"cpu_model": model, "logical_cpus_host": os.cpu_count(), "logical_cpus_visible": visible,
+                 "threads_used": threads,
                  "why": "the oracle's pool takes this process's CPU share (OMP_NUM_THREADS when set, else the "
                         "affinity mask)"},
         "single_thread": single,
@@ -348,6 +371,8 @@ def main():
             "counted_gbs": None if traffic is None else traffic / attn_avg_s / 1e9,
             "counted_frac": None if traffic is None else traffic / attn_avg_s / 1e9 / HBM_PEAK_GBS,
             "per_token_gbs": a_bytes / attn_avg_s / 1e9,
+            # the load instructions' address-unit time, spread evenly over the CUs
+            "gather_model": attn_gather_model(T, c_nonempty),
         },
     }
 

@@ -94,3 +94,19 @@ def test_host_cpu_share(monkeypatch):
 def test_stats():
     s = bench.stats([3.0, 1.0, 2.0, 10.0])
     assert s == {"n": 4, "median": 2.5, "min": 1.0, "max": 10.0, "mean": 4.0}
+
+
+def test_gather_model_counts_every_non_empty_wave():
+    """The load-instruction model: 8 x 21 + 16 x 21 + 2 x 85 + 4 x 66 + 21 = 959
+    address-unit cycles per (token, chunk) wave; at the long-context workload
+    (1984 x 33 non-empty waves over 256 CUs at 2.4 GHz) about 102 us."""
+    case = synth.long_ctx(layers=1)
+    _, c = bench.attn_bytes(case.ids, case.n_cells, case.T, case.H, case.D, case.n_chunks)
+    g = bench.attn_gather_model(case.T, c)
+    assert g["cycles_per_wave"] == 959
+    assert g["waves"] == 1984 * 33
+    assert abs(g["us"] - 1984 * 33 / 256 * 959 / 2400.0) < 1e-9
+    # an empty chunk issues no gathers, so it costs no modelled cycles
+    c2 = c.copy()
+    c2[:10] -= 1
+    assert bench.attn_gather_model(case.T, c2)["waves"] == g["waves"] - 10
