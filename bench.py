@@ -427,15 +427,23 @@ def main():
         for _ in range(2):
             qsa.qsa_attn_merge_gated(q0, kq0, vq0, ks0, vs0, ids, case.pos0, scale, gate, fout[0], gsum,
                                      stream=stream)
-        gev = [[ev(), ev()] for _ in range(args.steps)]
+        # gated and plain launches alternate on layer 0, so both see the same
+        # cache state and clocks
+        gev = [[ev(), ev(), ev()] for _ in range(args.steps)]
         for s_ in range(args.steps):
             gev[s_][0].record(stream)
+            qsa.qsa_attn_merge(q0, kq0, vq0, ks0, vs0, ids, case.pos0, scale, fout[1], stream=stream)
+            gev[s_][1].record(stream)
             qsa.qsa_attn_merge_gated(q0, kq0, vq0, ks0, vs0, ids, case.pos0, scale, gate, fout[0], gsum,
                                      stream=stream)
-            gev[s_][1].record(stream)
+            gev[s_][2].record(stream)
         torch.cuda.synchronize()
-        result["gated_fused_path"] = {"entry": "qsa_attn_merge_gated (fp32 gates, per-16 sums)",
-                                      "us_per_launch": stats([1e3 * e[0].elapsed_time(e[1]) for e in gev])}
+        g_us = [1e3 * e[1].elapsed_time(e[2]) for e in gev]
+        p_us = [1e3 * e[0].elapsed_time(e[1]) for e in gev]
+        result["gated_fused_path"] = {"entry": "qsa_attn_merge_gated (fp32 gates, per-16 sums), layer 0",
+                                      "us_per_launch": stats(g_us),
+                                      "plain_us_per_launch_alternating": stats(p_us),
+                                      "gated_over_plain_median": float(np.median(g_us) / np.median(p_us))}
         del fout, gate, gsum
 
     if not args.no_score:
