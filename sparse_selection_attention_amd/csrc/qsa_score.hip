@@ -11,9 +11,11 @@
 // and later cells are not written.
 //
 // Design on CDNA4. The head sum is linear, so sum_h (q_h . k) = (sum_h q_h) . k:
-// a 256-thread workgroup adds the heads of its 64 query rows once and then
+// a 512-thread workgroup adds the heads of its 64 query rows once and then
 // walks a run of consecutive 64-cell column tiles, each one a 64 x 64 x 128
-// contraction; each wave owns a 32 x 32 quadrant as four 16 x 16 accumulators.
+// contraction; each of its eight waves owns a 16 x 32 strip as two 16 x 16
+// accumulators, which holds it to 112 VGPRs, so two workgroups (16 waves)
+// share a CU.
 //
 // The contraction runs on the bf16 matrix cores (v_mfma_f32_16x16x32_bf16, 16
 // times the fp32 MFMA rate) with both operands split into two bf16 parts,
@@ -30,7 +32,7 @@
 //
 // The score scale multiplies the head-summed q once, before its split
 // (scale * (q . k) = (scale * q) . k up to rounding), and each wave keeps its
-// 32 rows' split operands in registers for the whole walk. K tiles are split
+// 16 rows' split operands in registers for the whole walk. K tiles are split
 // into bf16 parts as they are staged, into two LDS buffers used in turn: the
 // next tile is read into registers before the current one is multiplied and
 // staged into the other buffer after, so one barrier per tile suffices and
@@ -61,6 +63,7 @@ constexpr int kTile = 64;
 constexpr int kQPitch = kD + 4;  // fp32 q staging pitch (floats)
 constexpr int kKPitch = kD + 8;  // bf16 K tile pitch (elements): 272-byte rows, so the
                                  // 16 rows of one operand read start 4 banks apart
+constexpr int kScoreThreads = 512;  // 8 waves: 4 row strips of 16 x 2 column halves of 32
 constexpr int kSlots = 512;      // resident workgroups: 256 CUs x 2 (LDS and VGPRs allow two)
 constexpr int kQBytes = kTile * kQPitch * 4;
 constexpr int kKBytes = 2 * kTile * kKPitch * 2;          // one K tile: hi rows, then lo rows
@@ -101,22 +104,22 @@ __device__ inline void split4(const floatx4 &a, bf16x4 &hi, bf16x4 &lo)
     lo = (bf16x4){l[0][0], l[0][1], l[1][0], l[1][1]};
 }
 
-// the thread's staged K values (rows (tid >> 5) + 8i, column 4 * (tid & 31))
+// the thread's staged K values (rows (tid >> 5) + 16i, column 4 * (tid & 31))
 // split into bf16 high and low parts, into the K buffer at `buf`
-__device__ inline void stage_k(uint8_t *buf, const floatx4 (&kreg)[8], int tid)
+__device__ inline void stage_k(uint8_t *buf, const floatx4 (&kreg)[4], int tid)
 {
     __bf16 (*kh)[kKPitch] = (__bf16 (*)[kKPitch])buf;
     __bf16 (*kl)[kKPitch] = (__bf16 (*)[kKPitch])(buf + kTile * kKPitch * 2);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < 4; ++i) {
         bf16x4 h, l;
         split4(kreg[i], h, l);
-        *(bf16x4 *)&kh[(tid >> 5) + 8 * i][4 * (tid & 31)] = h;
-        *(bf16x4 *)&kl[(tid >> 5) + 8 * i][4 * (tid & 31)] = l;
+        *(bf16x4 *)&kh[(tid >> 5) + 16 * i][4 * (tid & 31)] = h;
+        *(bf16x4 *)&kl[(tid >> 5) + 16 * i][4 * (tid & 31)] = l;
     }
 }
 
-__global__ __launch_bounds__(256) void score_kernel(ScoreArgs a, int n_row_tiles, int run_len, int n_runs, int blocks_per_xcd)
+__global__ __launch_bounds__(kScoreThreads, 4) void score_kernel(ScoreArgs a, int n_row_tiles, int run_len, int n_runs, int blocks_per_xcd)
 {
     // two bf16 K buffers (hi rows, then lo rows); the fp32 q staging shares the second
     __shared__ __align__(16) uint8_t lds[kLdsBytes];
@@ -138,7 +141,7 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a, int n_row_tiles
 
     const int tid = threadIdx.x;
     // q rows of this tile, summed over heads, float4 per thread-step
-    for (int idx = tid; idx < kTile * (kD / 4); idx += 256) {
+    for (int idx = tid; idx < kTile * (kD / 4); idx += kScoreThreads) {
         const int row = idx >> 5, c4 = idx & 31;
         float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
         const int t = r0 + row;
@@ -166,16 +169,16 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a, int n_row_tiles
         *(float4 *)&sq[row][4 * c4] = acc;
     }
 
-    // K tile staging: thread tid moves 8 float4s, rows (tid >> 5) + 8i, column 4 * (tid & 31)
-    floatx4 kreg[8];
+    // K tile staging: thread tid moves 4 float4s, rows (tid >> 5) + 16i, column 4 * (tid & 31)
+    floatx4 kreg[4];
     auto fetch = [&](int ct) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
+        for (int i = 0; i < 4; ++i) {
             // a cell past the cache stages a copy of the last cell: a K row
             // feeds only its own score column, and such a column lies past
             // every row's causal edge (n_cells >= pos0 + T), so its value is
             // never written; the load stays unconditional, free of any branch
-            const int c = min(ct * kTile + (tid >> 5) + 8 * i, a.n_cells - 1);
+            const int c = min(ct * kTile + (tid >> 5) + 16 * i, a.n_cells - 1);
             kreg[i] = *(const floatx4 *)(a.k + (int64_t)c * kD + 4 * (tid & 31));
         }
     };
@@ -183,22 +186,21 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a, int n_row_tiles
 
     const int lane = tid & 63, w = tid >> 6;
     const int j = lane >> 4, c16 = lane & 15;
-    const int rq = 32 * (w >> 1), cq = 32 * (w & 1);   // this wave's quadrant
+    const int rq = 16 * (w >> 1), cq = 32 * (w & 1);   // this wave's 16 x 32 strip
+    const bool live = r0 + rq < a.T;                     // uniform: a strip past the last row only stages
 
-    // A operands, held for the whole walk: row rq + 16 mi + c16, dims 32 ks + 8j .. +7
+    // A operands, held for the whole walk: row rq + c16, dims 32 ks + 8j .. +7
     __syncthreads();
-    bf16x8 ah[2][4], al[2][4];
+    bf16x8 ah[4], al[4];
 #pragma unroll
-    for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            // the score scale goes on q here, once: scale * (q . k) = (scale * q) . k
-            const float *src = &sq[rq + 16 * mi + c16][32 * ks + 8 * j];
-            float4 u = *(const float4 *)src, v = *(const float4 *)(src + 4);
-            u.x *= a.scale; u.y *= a.scale; u.z *= a.scale; u.w *= a.scale;
-            v.x *= a.scale; v.y *= a.scale; v.z *= a.scale; v.w *= a.scale;
-            split8(u, v, ah[mi][ks], al[mi][ks]);
-        }
+    for (int ks = 0; ks < 4; ++ks) {
+        // the score scale goes on q here, once: scale * (q . k) = (scale * q) . k
+        const float *src = &sq[rq + c16][32 * ks + 8 * j];
+        float4 u = *(const float4 *)src, v = *(const float4 *)(src + 4);
+        u.x *= a.scale; u.y *= a.scale; u.z *= a.scale; u.w *= a.scale;
+        v.x *= a.scale; v.y *= a.scale; v.z *= a.scale; v.w *= a.scale;
+        split8(u, v, ah[ks], al[ks]);
+    }
     stage_k(lds, kreg, tid);                 // the first tile into buffer 0
     __syncthreads();                         // buffer 0 complete; the q staging is free
 
@@ -220,76 +222,63 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a, int n_row_tiles
         const __bf16 (*kh)[kKPitch] = (const __bf16 (*)[kKPitch])(lds + b * kKBytes);
         const __bf16 (*kl)[kKPitch] = (const __bf16 (*)[kKPitch])(lds + b * kKBytes + kTile * kKPitch * 2);
 
-        floatx4 acc[2][2];
+        floatx4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+        if (live) {
 #pragma unroll
-        for (int mi = 0; mi < 2; ++mi)
+            for (int ks = 0; ks < 4; ++ks) {
+                // B operand: cell cq + 16 ni + c16, dims 32 ks + 8j .. +7
+                bf16x8 bh[2], bl[2];
 #pragma unroll
-            for (int ni = 0; ni < 2; ++ni)
-                acc[mi][ni] = (floatx4){0.f, 0.f, 0.f, 0.f};
+                for (int ni = 0; ni < 2; ++ni) {
+                    bh[ni] = *(const bf16x8 *)&kh[cq + 16 * ni + c16][32 * ks + 8 * j];
+                    bl[ni] = *(const bf16x8 *)&kl[cq + 16 * ni + c16][32 * ks + 8 * j];
+                }
+                // the two accumulators are independent: interleave them between steps
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            // B operand: cell cq + 16 ni + c16, dims 32 ks + 8j .. +7
-            bf16x8 bh[2], bl[2];
+                for (int ni = 0; ni < 2; ++ni)
+                    acc[ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[ks], bh[ni], acc[ni], 0, 0, 0);
 #pragma unroll
-            for (int ni = 0; ni < 2; ++ni) {
-                bh[ni] = *(const bf16x8 *)&kh[cq + 16 * ni + c16][32 * ks + 8 * j];
-                bl[ni] = *(const bf16x8 *)&kl[cq + 16 * ni + c16][32 * ks + 8 * j];
+                for (int ni = 0; ni < 2; ++ni)
+                    acc[ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[ks], bl[ni], acc[ni], 0, 0, 0);
+#pragma unroll
+                for (int ni = 0; ni < 2; ++ni)
+                    acc[ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al[ks], bh[ni], acc[ni], 0, 0, 0);
             }
-            // the four accumulators are independent: interleave them between steps
-#pragma unroll
-            for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-                for (int ni = 0; ni < 2; ++ni)
-                    acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[mi][ks], bh[ni], acc[mi][ni], 0, 0, 0);
-#pragma unroll
-            for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-                for (int ni = 0; ni < 2; ++ni)
-                    acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[mi][ks], bl[ni], acc[mi][ni], 0, 0, 0);
-#pragma unroll
-            for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-                for (int ni = 0; ni < 2; ++ni)
-                    acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al[mi][ks], bh[ni], acc[mi][ni], 0, 0, 0);
         }
         // the staging waits for the reads: keep it behind the contraction
         __builtin_amdgcn_sched_barrier(0);
         stage_k(lds + (b ^ 1) * kKBytes, kreg, tid);   // unread after the last tile
 
         // D layout: lane (j, c16) holds rows 4j + r, column c16 of each 16 x 16 tile
-        if (full_rows && (int64_t)c0 + kTile - 1 <= first_causal) {
+        if (live && full_rows && (int64_t)c0 + kTile - 1 <= first_causal) {
             // every cell of the tile is causal for every row of the tile
 #pragma unroll
-            for (int mi = 0; mi < 2; ++mi)
+            for (int r = 0; r < 4; ++r) {
+                float *row = a.scores + (int64_t)(r0 + rq + 4 * j + r) * a.row_stride + c0 + cq + c16;
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    float *row = a.scores + (int64_t)(r0 + rq + 16 * mi + 4 * j + r) * a.row_stride + c0 + cq + c16;
+                for (int ni = 0; ni < 2; ++ni)
+                    __builtin_nontemporal_store(acc[ni][r], &row[16 * ni]);
+            }
+        } else if (live) {
 #pragma unroll
-                    for (int ni = 0; ni < 2; ++ni)
-                        __builtin_nontemporal_store(acc[mi][ni][r], &row[16 * ni]);
+            for (int r = 0; r < 4; ++r) {
+                const int t = r0 + rq + 4 * j + r;
+                if (t >= a.T)
+                    continue;
+                const int64_t p = (int64_t)a.pos0 + t;
+                int64_t tail_end = ((p + kTile) / kTile) * kTile;    // 64 * ceil((p + 1) / 64)
+                if (tail_end > a.row_stride)
+                    tail_end = a.row_stride;
+                float *row = a.scores + (int64_t)t * a.row_stride;
+#pragma unroll
+                for (int ni = 0; ni < 2; ++ni) {
+                    const int64_t c = c0 + cq + 16 * ni + c16;
+                    if (c <= p)
+                        __builtin_nontemporal_store(acc[ni][r], &row[c]);
+                    else if (c < tail_end)
+                        __builtin_nontemporal_store(a.dead, &row[c]);
                 }
-        } else {
-#pragma unroll
-            for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int t = r0 + rq + 16 * mi + 4 * j + r;
-                    if (t >= a.T)
-                        continue;
-                    const int64_t p = (int64_t)a.pos0 + t;
-                    int64_t tail_end = ((p + kTile) / kTile) * kTile;    // 64 * ceil((p + 1) / 64)
-                    if (tail_end > a.row_stride)
-                        tail_end = a.row_stride;
-                    float *row = a.scores + (int64_t)t * a.row_stride;
-#pragma unroll
-                    for (int ni = 0; ni < 2; ++ni) {
-                        const int64_t c = c0 + cq + 16 * ni + c16;
-                        if (c <= p)
-                            __builtin_nontemporal_store(acc[mi][ni][r], &row[c]);
-                        else if (c < tail_end)
-                            __builtin_nontemporal_store(a.dead, &row[c]);
-                    }
-                }
+            }
         }
         __syncthreads();                     // the next tile is staged; this buffer is free
     }
@@ -314,7 +303,7 @@ hipError_t launch_score(const ScoreArgs &a, hipStream_t stream)
     const int n_runs = (n_col_tiles + run_len - 1) / run_len;
     const int64_t blocks = (int64_t)n_runs * n_row_tiles;
     const int per_xcd = (int)((blocks + 7) / 8);
-    hipLaunchKernelGGL(score_kernel, dim3(8 * per_xcd), dim3(256), 0, stream, a, n_row_tiles, run_len, n_runs, per_xcd);
+    hipLaunchKernelGGL(score_kernel, dim3(8 * per_xcd), dim3(kScoreThreads), 0, stream, a, n_row_tiles, run_len, n_runs, per_xcd);
     return hipGetLastError();
 }
 
