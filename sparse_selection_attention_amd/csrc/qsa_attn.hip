@@ -250,8 +250,7 @@ __device__ inline float chunk_max(const float (&S)[4][4])
 #pragma unroll
         for (int r = 0; r < 4; ++r)
             mx = fmaxf(mx, S[b][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-    return fmaxf(mx, __shfl_xor(mx, 32, 64));
+    return xor32_max(xor16_max(mx));
 }
 
 // p = exp(S - ref) for head c16, and their sum over the chunk.
@@ -265,8 +264,7 @@ __device__ inline float chunk_probs(const float (&S)[4][4], float ref, float (&P
             P[b][r] = __builtin_amdgcn_exp2f((S[b][r] - ref) * kLog2e);  // exp(0) = 1 exactly
             lsum += P[b][r];
         }
-    lsum += __shfl_xor(lsum, 16, 64);
-    return lsum + __shfl_xor(lsum, 32, 64);
+    return xor32_sum(xor16_sum(lsum));
 }
 
 // O[tt] += p V over the chunk: O[tt] is heads 4j + r, dim 8*c16 + tt. The V

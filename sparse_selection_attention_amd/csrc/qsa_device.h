@@ -122,6 +122,43 @@ __device__ inline double xor_sum(double v, int lane_xor)
     return v + __shfl_xor(v, lane_xor, 64);
 }
 
+// Reductions over the lane pairs (l, l ^ 16) and (l, l ^ 32) through gfx950's
+// row-swap permutes, which exchange values inside the VALU where a shuffle
+// takes an LDS round trip. A swap of x with itself hands one lane of each pair
+// the pair's first value and the other lane the second; both lanes then
+// combine the same two values in the same order, so a pair ends with one
+// result (the same result a shuffle-based exchange gives: max and + commute).
+__device__ inline float xor16_max(float x)
+{
+    const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+__device__ inline float xor32_max(float x)
+{
+    const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+__device__ inline float xor16_sum(float x)
+{
+    const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+__device__ inline float xor32_sum(float x)
+{
+    const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+__device__ inline int xor16_max(int x)
+{
+    const auto p = __builtin_amdgcn_permlane16_swap((uint32_t)x, (uint32_t)x, false, false);
+    return max((int)p[0], (int)p[1]);
+}
+__device__ inline int xor32_max(int x)
+{
+    const auto p = __builtin_amdgcn_permlane32_swap((uint32_t)x, (uint32_t)x, false, false);
+    return max((int)p[0], (int)p[1]);
+}
+
 __device__ inline void wave_sync_lds()
 {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");

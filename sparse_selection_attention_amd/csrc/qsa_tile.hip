@@ -148,10 +148,10 @@ __device__ inline void load_raw(const AttnArgs &a, int c0, int tid, Raw &R)
 __device__ inline int group_max_exponent(const Raw &R)
 {
     int e = ((R.ok >> 2) & 1u) ? (int)((R.vs >> 10) & 31u) : 0;
-    e = max(e, __shfl_xor(e, 4, 64));
-    e = max(e, __shfl_xor(e, 8, 64));
-    e = max(e, __shfl_xor(e, 16, 64));
-    return max(e, __shfl_xor(e, 32, 64));
+    // lanes l, l + 4, l + 8, l + 12 of a row: two row rotations (by 4, then 8)
+    e = max(e, __builtin_amdgcn_update_dpp(0, e, 0x124, 0xf, 0xf, false));   // row_ror:4
+    e = max(e, __builtin_amdgcn_update_dpp(0, e, 0x128, 0xf, 0xf, false));   // row_ror:8
+    return xor32_max(xor16_max(e));
 }
 
 // The power of two that scale group g carries in this chunk: with eg the
@@ -355,8 +355,7 @@ __global__ __launch_bounds__(kTileThreads * G) void attn_tile_kernel(AttnArgs a,
 #pragma unroll
             for (int r = 0; r < 4; ++r)
                 mx = fmaxf(mx, S[b][r]);
-        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        mx = xor32_max(xor16_max(mx));
 
         // reference max for p, and (fused) the factor on what came before
         float ref, alpha = 1.0f;
@@ -377,8 +376,7 @@ __global__ __launch_bounds__(kTileThreads * G) void attn_tile_kernel(AttnArgs a,
                 P[b][r] = __builtin_amdgcn_exp2f(S[b][r] - ref);    // exp2(-inf) = 0, exp2(0) = 1
                 lsum += P[b][r];
             }
-        lsum += __shfl_xor(lsum, 16, 64);
-        lsum += __shfl_xor(lsum, 32, 64);
+        lsum = xor32_sum(xor16_sum(lsum));
         if constexpr (kFused) {
             // what came before: times alpha, and moved to this chunk's powers of two
             Lrun = fmaf(alpha, Lrun, lsum);
