@@ -267,12 +267,16 @@ __device__ inline float chunk_probs(const float (&S)[4][4], float ref, float (&P
     return xor32_sum(xor16_sum(lsum));
 }
 
-// O[tt] += p V over the chunk: O[tt] is heads 4j + r, dim 8*c16 + tt. The V
+// O[tt] += p V over the chunk: O[tt][r] is head 4j + r, dim 8*c16 + tt, or
+// with kByHead (the operands' roles swapped, so that the MFMA produces O^T) head
+// c16, dim 8*(4j + r) + tt: every value a lane holds then belongs to its own
+// head c16. The V
 // codes are converted times 2^-k_renorm (see stage_scales); V_hi is
 // the fp16 product with the scale and V_lo its exact residual from one fp16
 // fma (the product has at most 18 significant bits; when it is scaled by 2^-k
 // its lowest bits may fall below the fp16 grid, and V_lo then rounds by at
 // most 2^-25, i.e. 2^(k - 25) <= 2^-18 of the unscaled value).
+template <bool kByHead>
 __device__ inline void pv_accumulate(const float (&P)[4][4], const uint2 (&vraw)[2][8], const WaveLds &L, int j,
                                      int c16, int k_renorm, floatx4 (&O)[8])
 {
@@ -315,9 +319,15 @@ __device__ inline void pv_accumulate(const float (&P)[4][4], const uint2 (&vraw)
             }
             const half8 vb_hi = __builtin_bit_cast(half8, make_uint4(vh[0], vh[1], vh[2], vh[3]));
             const half8 vb_lo = __builtin_bit_cast(half8, make_uint4(vl[0], vl[1], vl[2], vl[3]));
-            O[tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa_hi, vb_hi, O[tt], 0, 0, 0);
-            O[tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa_hi, vb_lo, O[tt], 0, 0, 0);
-            O[tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa_lo, vb_hi, O[tt], 0, 0, 0);
+            if constexpr (kByHead) {
+                O[tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vb_hi, pa_hi, O[tt], 0, 0, 0);
+                O[tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vb_lo, pa_hi, O[tt], 0, 0, 0);
+                O[tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vb_hi, pa_lo, O[tt], 0, 0, 0);
+            } else {
+                O[tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa_hi, vb_hi, O[tt], 0, 0, 0);
+                O[tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa_hi, vb_lo, O[tt], 0, 0, 0);
+                O[tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa_lo, vb_hi, O[tt], 0, 0, 0);
+            }
         }
     }
 }
@@ -374,7 +384,7 @@ __global__ __launch_bounds__(64) void attn_kernel(AttnArgs a)
 #pragma unroll
     for (int tt = 0; tt < 8; ++tt)
         O[tt] = (floatx4){0.f, 0.f, 0.f, 0.f};
-    pv_accumulate(P, vraw, L, j, c16, kr, O);
+    pv_accumulate<false>(P, vraw, L, j, c16, kr, O);
 
     // ---- write the chunk record ----------------------------------------------
     if (kr != 0) {                  // take the V codes' power of two back out, exactly
@@ -436,7 +446,7 @@ __global__ __launch_bounds__(64 * kWavesMax) void attn_merge_kernel(AttnArgs a)
         copy_gate_rows(a, grows, t, w, nw, lane0);
 
     float Mrun = -INFINITY, Lrun = 0.0f;         // head c16
-    floatx4 O[8];                                // heads 4j + r, dim 8*c16 + tt
+    floatx4 O[8];                                // head c16, dims 8*(4j + r) + tt
 #pragma unroll
     for (int tt = 0; tt < 8; ++tt)
         O[tt] = (floatx4){0.f, 0.f, 0.f, 0.f};
@@ -468,14 +478,10 @@ __global__ __launch_bounds__(64 * kWavesMax) void attn_merge_kernel(AttnArgs a)
         float P[4][4];
         Lrun = fmaf(alpha, Lrun, chunk_probs(S, Mnew, P));
         Mrun = Mnew;
-        // rescale O by alpha of its own heads (held by lanes c16 = 4j + r)
+        // rescale O: every value this lane holds is of its own head c16
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const float ar = __shfl(alpha, 4 * j + r, 64);
-#pragma unroll
-            for (int tt = 0; tt < 8; ++tt)
-                O[tt][r] *= ar;
-        }
+        for (int tt = 0; tt < 8; ++tt)
+            O[tt] *= alpha;
         if (kr != 0) {              // the chunk's V codes carry 2^-k: put 2^k on p
             const float down = pow2f(kr);
 #pragma unroll
@@ -484,7 +490,7 @@ __global__ __launch_bounds__(64 * kWavesMax) void attn_merge_kernel(AttnArgs a)
                 for (int r = 0; r < 4; ++r)
                     P[b][r] *= down;
         }
-        pv_accumulate(P, vraw, L, j, c16, kr, O);
+        pv_accumulate<true>(P, vraw, L, j, c16, kr, O);
         wave_sync_lds();                         // the tile is rewritten by the next chunk
     }
 
@@ -493,16 +499,20 @@ __global__ __launch_bounds__(64 * kWavesMax) void attn_merge_kernel(AttnArgs a)
     const int j = lane0 >> 4, c16 = lane0 & 15;
     float *sM = (float *)L.ksc;                  // 16 floats
     float *sL = sM + 16;                         // 16 floats
-    float *sO = (float *)L.ktile;                // [16 heads][128 dims]
+    float *sO = (float *)L.ktile;                // [16 heads][128 dims], rows rotated (below)
     if (j == 0) {
         sM[c16] = Mrun;
         sL[c16] = Lrun;
     }
+    // head h's row holds its 32 granules of 4 dims rotated by h (granule g at
+    // (g + h) % 32), so the sixteen lanes of a row, one head each, write
+    // sixteen different bank groups
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        float *dst = sO + (4 * j + r) * kD + 8 * c16;
-        *(float4 *)dst = make_float4(O[0][r], O[1][r], O[2][r], O[3][r]);
-        *(float4 *)(dst + 4) = make_float4(O[4][r], O[5][r], O[6][r], O[7][r]);
+    for (int r = 0; r < 4; ++r) {               // head c16, dims 8(4j + r) .. +7
+        float *row = sO + c16 * kD;
+        const int g0 = 2 * (4 * j + r);
+        *(float4 *)(row + 4 * ((g0 + c16) & 31)) = make_float4(O[0][r], O[1][r], O[2][r], O[3][r]);
+        *(float4 *)(row + 4 * ((g0 + 1 + c16) & 31)) = make_float4(O[4][r], O[5][r], O[6][r], O[7][r]);
     }
     __syncthreads();
     for (int idx = threadIdx.x; idx < a.H * (kD / 4); idx += blockDim.x) {
@@ -523,7 +533,7 @@ __global__ __launch_bounds__(64 * kWavesMax) void attn_merge_kernel(AttnArgs a)
                     continue;
                 const float wv = __builtin_amdgcn_exp2f((mv - M) * kLog2e);
                 Ls = fmaf(wv, ((const float *)Lv.ksc)[16 + h], Ls);
-                const float4 ov = *(const float4 *)((const float *)Lv.ktile + h * kD + 4 * d4);
+                const float4 ov = *(const float4 *)((const float *)Lv.ktile + h * kD + 4 * ((d4 + h) & 31));
                 Os.x = fmaf(wv, ov.x, Os.x);
                 Os.y = fmaf(wv, ov.y, Os.y);
                 Os.z = fmaf(wv, ov.z, Os.z);
