@@ -29,8 +29,10 @@
 //     the cell's group scale, as the pages build the score from partials;
 //   * the chunk max and denominator are lane-local folds plus two cross-row
 //     exchanges, because the score tile already holds one head per lane column;
+//     the exchanges are gfx950's row-swap permutes, which stay in the VALU;
 //   * PV: v_mfma_f32_16x16x32_f16 with A = p (heads x 32 cells) straight from
-//     the score tile's registers, and B = V rows dequantised to fp16. Both sides
+//     the score tile's registers, and B = V rows dequantised to fp16 (the fused
+//     kernel swaps the two, so that each lane accumulates its own head's dims). Both sides
 //     are split into fp16 high and low parts and contracted as
 //     hi*hi + hi*lo + lo*hi, so the products carry about 22 bits:
 //       - vq * vsc has at most 18 significant bits, so V = V_hi + V_lo exactly,

@@ -29,7 +29,8 @@
 //   * QK: v_mfma_f32_16x16x32_f16 with A = 16 cells x 32 dims of one scale
 //     group and B = the wave's 16 q rows, one fp32 partial per scale group,
 //     weighted by the cell's group scale; a lane then holds 16 of its row's
-//     64 scores, so the row max and sum are lane folds plus two exchanges.
+//     64 scores, so the row max and sum are lane folds plus two exchanges
+//     (row-swap permutes, in the VALU).
 //     Scores are kept in log2 units (the softmax scale is applied times
 //     log2(e)), so p = exp2(S - max) needs no multiply;
 //   * causality is a per-row mask: cell c counts for row r iff
