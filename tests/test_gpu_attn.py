@@ -415,3 +415,38 @@ def test_merge_rows_without_records_give_plus_zero(C):
     qsa.qsa_merge(part, C, out)
     torch.cuda.synchronize()
     assert np.all(out.cpu().numpy().view(np.uint16) == 0)
+
+
+@pytest.mark.parametrize("implicit", [False, True])
+def test_token_pieces_match_one_call(implicit):
+    """A layer run as several calls on consecutive token ranges (pos0 moved by
+    each range's first token) gives the one-call output bit for bit: the way a
+    caller keeps one call's chunk records inside the Infinity Cache."""
+    import torch
+    import sparse_selection_attention_amd as qsa
+    from gpu_util import to_dev
+    case = synth.mid(layers=1) if not implicit else synth.prompt_start(implicit=True)
+    L = case.layers[0]
+    T, H, D = L.q.shape
+    q, kq, vq, ksc, vsc = (to_dev(x) for x in (L.q, L.kq, L.vq, L.ksc, L.vsc))
+    ids = None if implicit else to_dev(case.ids)
+    C = qsa.chunk_count(ids, case.pos0, T)
+    part = qsa.alloc_part(T, H, D, C)
+    full = torch.empty(T, H, D, dtype=torch.float16, device=q.device)
+    qsa.qsa_attn(q, kq, vq, ksc, vsc, ids, case.pos0, float(case.scale), part)
+    qsa.qsa_merge(part, C, full)
+    pieces = torch.full((T, H, D), float("nan"), dtype=torch.float16, device=q.device)
+    for t0, t1 in ((0, 700), (700, 701), (701, 1300), (1300, T)):
+        if implicit:
+            # implicit rows: a piece's rows are cells 0 .. pos0 + t of the same cache
+            n = t1 - t0
+            Cp = qsa.chunk_count(None, case.pos0 + t0, n)
+            pp = qsa.alloc_part(n, H, D, Cp)
+            qsa.qsa_attn(q[t0:t1], kq, vq, ksc, vsc, None, case.pos0 + t0, float(case.scale), pp)
+            qsa.qsa_merge(pp, Cp, pieces[t0:t1])
+        else:
+            pp = qsa.alloc_part(t1 - t0, H, D, C)
+            qsa.qsa_attn(q[t0:t1], kq, vq, ksc, vsc, ids[t0:t1], case.pos0 + t0, float(case.scale), pp)
+            qsa.qsa_merge(pp, C, pieces[t0:t1])
+    torch.cuda.synchronize()
+    assert torch.equal(full.view(torch.int16), pieces.view(torch.int16))
