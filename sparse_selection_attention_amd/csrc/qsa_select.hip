@@ -48,6 +48,39 @@ constexpr int kLDec = kLTot + kBins * 4;               // uint[2][2]: digit, cou
 constexpr int kLCnt1 = kLDec + 16;                     // uint[3 passes][256]: single-copy histograms
 constexpr int kSelLds = kLCnt1 + 3 * kBins * 4;
 
+// Inclusive prefix sum over the 64 lanes of a wave in six DPP steps: shifts by
+// 1, 2, 4 and 8 lanes inside each 16-lane row, then each row adds the totals
+// of the rows before it through the row broadcasts of lanes 15 and 31. All in
+// the VALU; a shuffle-based scan takes an LDS round trip per step.
+__device__ inline uint32_t wave_prefix_sum(uint32_t v)
+{
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xf, 0xf, false);   // row_shr:1
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xf, 0xf, false);   // row_shr:2
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xf, 0xf, false);   // row_shr:4
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xf, 0xf, false);   // row_shr:8
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xa, 0xf, false);   // row_bcast:15 to rows 1, 3
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xc, 0xf, false);   // row_bcast:31 to rows 2, 3
+    return v;
+}
+
+// Inclusive suffix sum over the lanes (lane l: lanes l .. 63), from the prefix
+// sum and the wave total.
+__device__ inline uint32_t wave_suffix_sum(uint32_t v)
+{
+    const uint32_t pre = wave_prefix_sum(v);
+    const uint32_t total = (uint32_t)__builtin_amdgcn_readlane((int)pre, 63);
+    return total - pre + v;
+}
+
+// Sum over aligned groups of `parts` lanes (2 or 4) by DPP quad permutes.
+__device__ inline uint32_t quad_group_sum(uint32_t v, int parts)
+{
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xf, 0xf, false);    // lane ^ 1
+    if (parts == 4)
+        v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xf, 0xf, false);   // lane ^ 2
+    return v;
+}
+
 // Order-preserving key: larger score, larger key. Non-negative scores map to
 // b | 2^31 (+0 to 2^31); negative ones to 2^32 - b, so -0 (b = 2^31) meets
 // +0 at 2^31 and the most negative bit pattern maps to 1, above the key 0
@@ -122,13 +155,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(8))) void se
             for (int i = 0; i < 4; ++i)
                 b[i] = hist[4 * lane + i];
             const uint32_t mine = b[0] + b[1] + b[2] + b[3];
-            uint32_t suf = mine;                         // bins 4l .. 255
-#pragma unroll
-            for (int d = 1; d < 64; d <<= 1) {
-                const uint32_t o = __shfl_down(suf, d, 64);
-                if (lane + d < 64)
-                    suf += o;
-            }
+            const uint32_t suf = wave_suffix_sum(mine);  // bins 4l .. 255
             const uint32_t above_lane = suf - mine;      // bins 4l+4 .. 255
             if (above_lane < k_left && suf >= k_left) {
                 uint32_t acc = above_lane;
@@ -170,9 +197,8 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(8))) void se
             const uint4 v = src[i];
             sum += v.x + v.y + v.z + v.w;
         }
-#pragma unroll
-        for (int d = 1; d < kParts; d <<= 1)
-            sum += __shfl_xor(sum, d, 64);
+        static_assert(kParts == 2 || kParts == 4, "a bin's copies are summed by 2 or 4 lanes");
+        sum = quad_group_sum(sum, kParts);
         if (part == 0)
             tot[bin] = sum;
     }
@@ -229,13 +255,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(8))) void se
     }
     // counts packed as (above << 16) | equal: each is at most 32768 over the row
     const uint32_t own = ((uint32_t)__popc(gt32) << 16) | (uint32_t)__popc(eq32);
-    uint32_t inc = own;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-        const uint32_t o = __shfl_up(inc, d, 64);
-        if (lane >= d)
-            inc += o;
-    }
+    const uint32_t inc = wave_prefix_sum(own);
     uint32_t *wsum = tot;                                // [kSelWaves] wave totals
     if (lane == 63)
         wsum[w] = inc;
@@ -317,9 +337,8 @@ __global__ __launch_bounds__(kStreamThreads) void select_stream_kernel(SelectArg
             const uint4 v = src[i];
             sum += v.x + v.y + v.z + v.w;
         }
-#pragma unroll
-        for (int d = 1; d < kParts; d <<= 1)
-            sum += __shfl_xor(sum, d, 64);
+        static_assert(kParts == 2 || kParts == 4, "a bin's copies are summed by 2 or 4 lanes");
+        sum = quad_group_sum(sum, kParts);
         if (part == 0)
             tot[bin] = sum;
     }
@@ -344,13 +363,7 @@ __global__ __launch_bounds__(kStreamThreads) void select_stream_kernel(SelectArg
             for (int i = 0; i < 4; ++i)
                 b[i] = hist[4 * lane + i];
             const uint32_t mine = b[0] + b[1] + b[2] + b[3];
-            uint32_t suf = mine;
-#pragma unroll
-            for (int d = 1; d < 64; d <<= 1) {
-                const uint32_t o = __shfl_down(suf, d, 64);
-                if (lane + d < 64)
-                    suf += o;
-            }
+            const uint32_t suf = wave_suffix_sum(mine);
             const uint32_t above_lane = suf - mine;
             if (above_lane < k_left && suf >= k_left) {
                 uint32_t acc = above_lane;
@@ -402,13 +415,7 @@ __global__ __launch_bounds__(kStreamThreads) void select_stream_kernel(SelectArg
         const uint4 wd = words[tid >> 1];
         const uint32_t gt32 = (tid & 1) ? wd.y : wd.x, eq32 = (tid & 1) ? wd.w : wd.z;
         const uint32_t own = ((uint32_t)__popc(gt32) << 16) | (uint32_t)__popc(eq32);
-        uint32_t inc = own;
-#pragma unroll
-        for (int d = 1; d < 64; d <<= 1) {
-            const uint32_t o = __shfl_up(inc, d, 64);
-            if (lane >= d)
-                inc += o;
-        }
+        const uint32_t inc = wave_prefix_sum(own);
         if (lane == 63)
             wsum[w] = inc;
         __syncthreads();
