@@ -60,9 +60,14 @@ __global__ __launch_bounds__(64 * kWaves) void merge_kernel(MergeArgs a)
         if (k < a.C)
             M = fmaxf(M, a.m[base + (int64_t)k * a.H]);
     }
-#pragma unroll
-    for (int s = 16; s >= 1; s >>= 1)
-        M = fmaxf(M, __shfl_xor(M, s, 64));
+    // max over the 32 lanes of this half-wave, in the VALU: lane ^ 16 by the
+    // row-swap permute, then lanes 8 and 4 apart by row rotations and lanes 2
+    // and 1 apart by quad permutes
+    M = dev::xor16_max(M);
+    M = fmaxf(M, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(M), 0x128, 0xf, 0xf, false)));  // row_ror:8
+    M = fmaxf(M, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(M), 0x124, 0xf, 0xf, false)));  // row_ror:4
+    M = fmaxf(M, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(M), 0x4E, 0xf, 0xf, false)));   // lane ^ 2
+    M = fmaxf(M, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(M), 0xB1, 0xf, 0xf, false)));   // lane ^ 1
 
     float4 y = make_float4(0.f, 0.f, 0.f, 0.f);  // +0 when no chunk of the row had a valid slot
     if (M != -INFINITY) {
