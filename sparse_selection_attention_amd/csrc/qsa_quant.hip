@@ -65,7 +65,6 @@ __device__ inline uint32_t pack4(float4 x, float s, float r)
 __global__ __launch_bounds__(256) void quant_kernel(QuantArgs a)
 {
     const int tid = threadIdx.x;
-    const int lane = tid & 63;
     const int64_t task = (int64_t)blockIdx.x * kRowsPerBlock + (tid >> 3);
     // all 8 threads of a row share `task`, so a row is wholly in or out
     const bool active = task < 2 * (int64_t)a.n_rows;
@@ -87,18 +86,22 @@ __global__ __launch_bounds__(256) void quant_kernel(QuantArgs a)
             x[i] = make_float4(0.f, 0.f, 0.f, 0.f);
     }
     float amax = fmaxf(fmaxf(absmax4(x[0]), absmax4(x[1])), fmaxf(absmax4(x[2]), absmax4(x[3])));
-    amax = fmaxf(amax, __shfl_xor(amax, 1, 64));        // the two threads of a group
+    // the two threads of a group (lanes 2i, 2i + 1): a quad permute, in the VALU
+    amax = fmaxf(amax, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(amax), 0xB1, 0xf, 0xf, false)));
     const _Float16 s16 = (_Float16)__fdiv_rn(amax, 127.0f);    // binary32 quotient, then RNE to fp16
     const float s = (float)s16;
     const float rcp = (s > 0.0f && s < INFINITY) ? __builtin_amdgcn_rcpf(s) : 0.0f;
 
     const uint4 codes = make_uint4(pack4(x[0], s, rcp), pack4(x[1], s, rcp), pack4(x[2], s, rcp),
                                    pack4(x[3], s, rcp));
-    // the row's four scales, from its threads 0, 2, 4 and 6
+    // the row's four scales, from its threads 0, 2, 4 and 6, for thread 0 (lane
+    // 8i, whose row threads are lanes 8i .. 8i + 7 of one 16-lane DPP row):
+    // shifts of the lanes 2, 4 and 6 above it, in the VALU
     const uint32_t sbits = (uint32_t)__builtin_bit_cast(uint16_t, s16);
-    const int row_lane = lane & ~7;
-    const uint32_t g0 = __shfl(sbits, row_lane + 0, 64), g1 = __shfl(sbits, row_lane + 2, 64);
-    const uint32_t g2 = __shfl(sbits, row_lane + 4, 64), g3 = __shfl(sbits, row_lane + 6, 64);
+    const uint32_t g0 = sbits;
+    const uint32_t g1 = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)sbits, 0x102, 0xf, 0xf, false);   // row_shl:2
+    const uint32_t g2 = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)sbits, 0x104, 0xf, 0xf, false);   // row_shl:4
+    const uint32_t g3 = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)sbits, 0x106, 0xf, 0xf, false);   // row_shl:6
     if (active) {
         const int64_t cell = (int64_t)a.cell0 + r;
         *(uint4 *)((is_v ? a.vq : a.kq) + cell * kD + e0) = codes;
