@@ -291,14 +291,12 @@ __device__ inline void pv_accumulate(const float (&P)[4][4], const uint2 (&vraw)
 #pragma unroll
     for (int ks2 = 0; ks2 < 2; ++ks2) {
         // A operand: p of slots s = cells 32ks + 16(s/4) + 4j + s%4, as hi + lo
-        half8 pa_hi, pa_lo;
+        float pv[8];
 #pragma unroll
-        for (int s = 0; s < 8; ++s) {
-            const float pv = P[2 * ks2 + (s >> 2)][s & 3];
-            const _Float16 hi = (_Float16)pv;
-            pa_hi[s] = hi;
-            pa_lo[s] = (_Float16)(pv - (float)hi);
-        }
+        for (int s = 0; s < 8; ++s)
+            pv[s] = P[2 * ks2 + (s >> 2)][s & 3];
+        half8 pa_hi, pa_lo;
+        split_half8(pv, pa_hi, pa_lo);
         // V scales of the slot pairs (s, s+1): adjacent cells, one dword each
         half2v sc[4];
 #pragma unroll

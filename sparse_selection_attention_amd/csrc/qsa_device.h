@@ -89,6 +89,31 @@ __device__ inline half8 i8x8_to_half8(uint2 v)
     return __builtin_bit_cast(half8, make_uint4(r[0], r[1], r[2], r[3]));
 }
 
+// v = hi + lo for eight fp32 values: hi the fp16 rounding of v (converted two
+// values per instruction), lo the fp16 rounding of the residual v - hi. The
+// residual is exact in fp32 for every v, so one fma that reads hi as fp16
+// gives it without converting hi back: the same bits as the plain
+// subtraction, in one instruction instead of two.
+__device__ inline void split_half8(const float (&v)[8], half8 &hi, half8 &lo)
+{
+    // -1 kept opaque, so that the fma is not rewritten into a subtraction
+    // (which would need hi converted back to fp32 first)
+    float m1 = -1.0f;
+    asm volatile("" : "+s"(m1));
+#pragma unroll
+    for (int s = 0; s < 8; s += 2) {
+        // the pair is converted once, and the fmas read its two halves
+        uint32_t hp = __builtin_bit_cast(uint32_t, (half2v){(_Float16)v[s], (_Float16)v[s + 1]});
+        asm volatile("" : "+v"(hp));
+        const _Float16 h0 = __builtin_bit_cast(_Float16, (uint16_t)(hp & 0xffffu));
+        const _Float16 h1 = __builtin_bit_cast(_Float16, (uint16_t)(hp >> 16));
+        hi[s] = h0;
+        hi[s + 1] = h1;
+        lo[s] = (_Float16)__builtin_fmaf((float)h0, m1, v[s]);
+        lo[s + 1] = (_Float16)__builtin_fmaf((float)h1, m1, v[s + 1]);
+    }
+}
+
 // sigmoid(g) = 1 / (1 + exp(-g)) in fp32, with a correctly rounded division:
 // sigmoid(0) = 1/2, sigmoid(+inf) = 1 and sigmoid(-inf) = +0 exactly, and a
 // NaN gate stays NaN. exp(-g) overflows to +inf below g = -88.7, where the

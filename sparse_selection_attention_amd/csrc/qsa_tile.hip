@@ -206,7 +206,10 @@ __device__ inline void stage_tiles(uint8_t *lds, int tid, const Raw &R, const in
 
 // Scores of the chunk's 64 cells for this lane's row, in log2 units: the four
 // group partials of QK weighted by the cells' K scales, times kmul (the
-// softmax scale times log2(e)); cells past the row's last valid cell get -inf.
+// softmax scale times log2(e)); with kMask, cells past the row's last valid
+// cell get -inf (chunks that lie wholly inside every row's causal range skip
+// the test).
+template <bool kMask>
 __device__ inline void qk_scores(const uint8_t *lds, const half8 (&qop)[4], int j, int c16, int c0, int lim,
                                  float kmul, float (&S)[4][4])
 {
@@ -227,7 +230,7 @@ __device__ inline void qk_scores(const uint8_t *lds, const half8 (&qop)[4], int 
             dot = __builtin_fmaf(acc[1][r], half_bits_to_float(kb.x >> 16), dot);
             dot = __builtin_fmaf(acc[2][r], half_bits_to_float(kb.y & 0xffffu), dot);
             dot = __builtin_fmaf(acc[3][r], half_bits_to_float(kb.y >> 16), dot);
-            S[b][r] = c0 + cell <= lim ? kmul * dot : -INFINITY;
+            S[b][r] = (!kMask || c0 + cell <= lim) ? kmul * dot : -INFINITY;
         }
     }
 }
@@ -240,14 +243,12 @@ __device__ inline void pv_accumulate(const uint8_t *lds, const float (&P)[4][4],
     for (int ks = 0; ks < 2; ++ks) {
         // p of positions 32ks + 8j + s (cells 32ks + 16(s/4) + 4j + s%4) as
         // fp16 high and low parts, p = hi + lo to within 2^-22
-        half8 ph, pl;
+        float pv[8];
 #pragma unroll
-        for (int s = 0; s < 8; ++s) {
-            const float pv = P[2 * ks + (s >> 2)][s & 3];
-            const _Float16 hi = (_Float16)pv;
-            ph[s] = hi;
-            pl[s] = (_Float16)(pv - (float)hi);
-        }
+        for (int s = 0; s < 8; ++s)
+            pv[s] = P[2 * ks + (s >> 2)][s & 3];
+        half8 ph, pl;
+        split_half8(pv, ph, pl);
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
             // those positions' scales of group g (times 2^kg): B = p * scale as
@@ -302,6 +303,10 @@ __global__ __launch_bounds__(kTileThreads * G) void attn_tile_kernel(AttnArgs a,
     const int h = row_ok ? row - t * a.H : 0;
     const int lim = row_ok ? (int)min((int64_t)a.pos0 + t, (int64_t)a.n_cells - 1) : -1;   // last valid cell
     const float kmul = a.scale * kLog2e;        // scores in log2 units
+    // the wave's smallest last valid cell: lane 0 holds the wave's first row
+    // (rows past the end have lim = -1, and a wave whose first row is past
+    // the end masks every chunk)
+    const int lim_w = __builtin_amdgcn_readfirstlane(lim);
 
     half8 qop[4];
 #pragma unroll
@@ -349,7 +354,10 @@ __global__ __launch_bounds__(kTileThreads * G) void attn_tile_kernel(AttnArgs a,
 
         // ---- QK: S[b][r] is cell 16b + 4j + r of this lane's row, log2 units ---
         float S[4][4];
-        qk_scores(lds, qop, j, c16, c0, lim, kmul, S);
+        if (c0 + kChunk - 1 <= lim_w)           // uniform: every cell counts for every row of the wave
+            qk_scores<false>(lds, qop, j, c16, c0, lim, kmul, S);
+        else
+            qk_scores<true>(lds, qop, j, c16, c0, lim, kmul, S);
         float mx = -INFINITY;
 #pragma unroll
         for (int b = 0; b < 4; ++b)
