@@ -213,9 +213,18 @@ __device__ inline int stage_scales(const WaveLds &L, int lane, uint2 ks, uint2 v
 // 2^k as a float, for 0 <= k <= 7
 __device__ inline float pow2f(int k) { return __int_as_float((127 + k) << 23); }
 
+// -0, from an argument the compiler cannot see through (n_cells >= 0). The
+// first product of each score is an fma with it, which reads the fp16 scale
+// directly (x + -0 = x for every x, so it is the product's value), where a
+// constant -0 would be folded back into a multiply.
+__device__ inline float opaque_neg_zero(const AttnArgs &a)
+{
+    return __int_as_float((int)(0x80000000u | (uint32_t)(a.n_cells >> 31)));
+}
+
 // Scaled scores of the chunk: S[b][r] is cell 16b + 4j + r, head c16; empty
 // slots get -inf.
-__device__ inline void chunk_scores(float scale, const WaveLds &L, const half8 (&qop)[4], uint64_t mask, int j,
+__device__ inline void chunk_scores(float scale, float nz, const WaveLds &L, const half8 (&qop)[4], uint64_t mask, int j,
                                     int c16, float (&S)[4][4])
 {
     const floatx4 zero = {0.f, 0.f, 0.f, 0.f};
@@ -233,7 +242,7 @@ __device__ inline void chunk_scores(float scale, const WaveLds &L, const half8 (
         for (int r = 0; r < 4; ++r) {
             const int cell = 16 * b + 4 * j + r;
             const uint2 kb = L.ksc[cell];
-            float dot = acc[0][r] * half_bits_to_float(kb.x & 0xffffu);
+            float dot = __builtin_fmaf(acc[0][r], half_bits_to_float(kb.x & 0xffffu), nz);
             dot = __builtin_fmaf(acc[1][r], half_bits_to_float(kb.x >> 16), dot);
             dot = __builtin_fmaf(acc[2][r], half_bits_to_float(kb.y & 0xffffu), dot);
             dot = __builtin_fmaf(acc[3][r], half_bits_to_float(kb.y >> 16), dot);
@@ -376,7 +385,7 @@ __global__ __launch_bounds__(64) void attn_kernel(AttnArgs a)
 
     const int kr = stage_scales(L, lane, ks, vs);
     float S[4][4];
-    chunk_scores(a.scale, L, qop, mask, j, c16, S);
+    chunk_scores(a.scale, opaque_neg_zero(a), L, qop, mask, j, c16, S);
     const float mx = chunk_max(S);
     float P[4][4];
     const float lsum = chunk_probs(S, mx, P);
@@ -472,7 +481,7 @@ __global__ __launch_bounds__(64 * kWavesMax) void attn_merge_kernel(AttnArgs a)
         half8 qop[4];
         q_operand(a, qrows, j, c16, qop);
         float S[4][4];
-        chunk_scores(a.scale, L, qop, mask, j, c16, S);
+        chunk_scores(a.scale, opaque_neg_zero(a), L, qop, mask, j, c16, S);
         const float Mnew = fmaxf(Mrun, chunk_max(S));
         const float alpha = __builtin_amdgcn_exp2f((Mrun - Mnew) * kLog2e);   // 0 for the first chunk
         float P[4][4];

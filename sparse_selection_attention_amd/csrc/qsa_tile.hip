@@ -211,7 +211,7 @@ __device__ inline void stage_tiles(uint8_t *lds, int tid, const Raw &R, const in
 // the test).
 template <bool kMask>
 __device__ inline void qk_scores(const uint8_t *lds, const half8 (&qop)[4], int j, int c16, int c0, int lim,
-                                 float kmul, float (&S)[4][4])
+                                 float kmul, float nz, float (&S)[4][4])
 {
     const floatx4 zero = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -226,7 +226,7 @@ __device__ inline void qk_scores(const uint8_t *lds, const half8 (&qop)[4], int 
         for (int r = 0; r < 4; ++r) {
             const int cell = 16 * b + 4 * j + r;
             const uint2 kb = *(const uint2 *)(lds + kLKs + cell * 8);
-            float dot = acc[0][r] * half_bits_to_float(kb.x & 0xffffu);
+            float dot = __builtin_fmaf(acc[0][r], half_bits_to_float(kb.x & 0xffffu), nz);
             dot = __builtin_fmaf(acc[1][r], half_bits_to_float(kb.x >> 16), dot);
             dot = __builtin_fmaf(acc[2][r], half_bits_to_float(kb.y & 0xffffu), dot);
             dot = __builtin_fmaf(acc[3][r], half_bits_to_float(kb.y >> 16), dot);
@@ -303,6 +303,11 @@ __global__ __launch_bounds__(kTileThreads * G) void attn_tile_kernel(AttnArgs a,
     const int h = row_ok ? row - t * a.H : 0;
     const int lim = row_ok ? (int)min((int64_t)a.pos0 + t, (int64_t)a.n_cells - 1) : -1;   // last valid cell
     const float kmul = a.scale * kLog2e;        // scores in log2 units
+    // -0, from an argument the compiler cannot see through (n_cells >= 0): the
+    // first product of each score is an fma with it, which reads the fp16
+    // scale directly (x + -0 = x for every x, so it is the product's value),
+    // where a constant -0 would be folded back into a multiply
+    const float nz = __int_as_float((int)(0x80000000u | (uint32_t)(a.n_cells >> 31)));
     // the wave's smallest last valid cell: lane 0 holds the wave's first row
     // (rows past the end have lim = -1, and a wave whose first row is past
     // the end masks every chunk)
@@ -355,9 +360,9 @@ __global__ __launch_bounds__(kTileThreads * G) void attn_tile_kernel(AttnArgs a,
         // ---- QK: S[b][r] is cell 16b + 4j + r of this lane's row, log2 units ---
         float S[4][4];
         if (c0 + kChunk - 1 <= lim_w)           // uniform: every cell counts for every row of the wave
-            qk_scores<false>(lds, qop, j, c16, c0, lim, kmul, S);
+            qk_scores<false>(lds, qop, j, c16, c0, lim, kmul, nz, S);
         else
-            qk_scores<true>(lds, qop, j, c16, c0, lim, kmul, S);
+            qk_scores<true>(lds, qop, j, c16, c0, lim, kmul, nz, S);
         float mx = -INFINITY;
 #pragma unroll
         for (int b = 0; b < 4; ++b)
