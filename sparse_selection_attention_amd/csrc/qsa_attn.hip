@@ -64,7 +64,8 @@ constexpr int kWavesMax = 8;               // over few chunks (one wave each), o
 // LDS layout: one wave region per wave, then (fused workgroup only) the q rows
 constexpr int kKTileBytes = kChunk * kD;                 // 8 KB of K rows per wave
 constexpr int kWaveBytes = kKTileBytes + kChunk * 8      // K tile, K scales (fp16 x 4)
-                           + kChunk * 8 + kChunk * 4;    // V scales (group-major), cell ids
+                           + kChunk * 8 + kChunk * 4     // V scales (group-major), cell ids
+                           + kChunk * 4;                 // score penalties
 // (gated calls only) then the token's fp32 gate rows
 constexpr int attn_lds_bytes(int nw, int H, bool gated) { return nw * kWaveBytes + H * kD * 2 + (gated ? H * kD * 4 : 0); }
 
@@ -86,13 +87,14 @@ struct WaveLds {
     uint2 *ksc;          // [64] cells x 4 fp16 K scales
     uint16_t *vsc;       // [4 groups][64 cells] fp16 V scales
     int32_t *id;         // [64] cell ids (0 for empty slots)
+    float *pen;          // [64] added to the scaled score: -0 for a valid slot, -inf for an empty one
 };
 
 __device__ inline WaveLds wave_lds(uint8_t *lds, int w)
 {
     uint8_t *base = lds + w * kWaveBytes;
     return WaveLds{base, (uint2 *)(base + kKTileBytes), (uint16_t *)(base + kKTileBytes + kChunk * 8),
-                   (int32_t *)(base + kKTileBytes + kChunk * 16)};
+                   (int32_t *)(base + kKTileBytes + kChunk * 16), (float *)(base + kKTileBytes + kChunk * 20)};
 }
 
 // The token's q rows (H x 256 B) into LDS: 16-byte granules, head h's logical
@@ -153,6 +155,7 @@ __device__ inline uint64_t issue_chunk(const AttnArgs &a, const WaveLds &L, int3
     const uint64_t mask = __ballot(valid);
 
     L.id[lane] = sid;
+    L.pen[lane] = valid ? -0.0f : -INFINITY;
     wave_sync_lds();
     ks = make_uint2(0u, 0u);
     vs = make_uint2(0u, 0u);
@@ -222,10 +225,12 @@ __device__ inline float opaque_neg_zero(const AttnArgs &a)
     return __int_as_float((int)(0x80000000u | (uint32_t)(a.n_cells >> 31)));
 }
 
-// Scaled scores of the chunk: S[b][r] is cell 16b + 4j + r, head c16; empty
-// slots get -inf.
-__device__ inline void chunk_scores(float scale, float nz, const WaveLds &L, const half8 (&qop)[4], uint64_t mask, int j,
-                                    int c16, float (&S)[4][4])
+// Scaled scores of the chunk: S[b][r] is cell 16b + 4j + r, head c16. The
+// slot's penalty is the addend of the scaling fma: + -0 leaves the product as
+// it is (signed zeros included), + -inf makes an empty slot's score -inf (its
+// product is finite: the slot reads row 0 with zero scales).
+__device__ inline void chunk_scores(float scale, float nz, const WaveLds &L, const half8 (&qop)[4], int j, int c16,
+                                    float (&S)[4][4])
 {
     const floatx4 zero = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -238,6 +243,8 @@ __device__ inline void chunk_scores(float scale, float nz, const WaveLds &L, con
             const uint2 kr = *(const uint2 *)(L.ktile + ktile_offset(row, 2 * g + (j >> 1)) + 8 * (j & 1));
             acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(i8x8_to_half8(kr), qop[g], zero, 0, 0, 0);
         }
+        const float4 p4 = *(const float4 *)(L.pen + 16 * b + 4 * j);   // cells 16b + 4j .. +3
+        const float pen[4] = {p4.x, p4.y, p4.z, p4.w};
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int cell = 16 * b + 4 * j + r;
@@ -246,8 +253,7 @@ __device__ inline void chunk_scores(float scale, float nz, const WaveLds &L, con
             dot = __builtin_fmaf(acc[1][r], half_bits_to_float(kb.x >> 16), dot);
             dot = __builtin_fmaf(acc[2][r], half_bits_to_float(kb.y & 0xffffu), dot);
             dot = __builtin_fmaf(acc[3][r], half_bits_to_float(kb.y >> 16), dot);
-            const float sv = scale * dot;
-            S[b][r] = ((mask >> cell) & 1ull) ? sv : -INFINITY;
+            S[b][r] = __builtin_fmaf(scale, dot, pen[r]);
         }
     }
 }
@@ -385,7 +391,7 @@ __global__ __launch_bounds__(64) void attn_kernel(AttnArgs a)
 
     const int kr = stage_scales(L, lane, ks, vs);
     float S[4][4];
-    chunk_scores(a.scale, opaque_neg_zero(a), L, qop, mask, j, c16, S);
+    chunk_scores(a.scale, opaque_neg_zero(a), L, qop, j, c16, S);
     const float mx = chunk_max(S);
     float P[4][4];
     const float lsum = chunk_probs(S, mx, P);
@@ -481,7 +487,7 @@ __global__ __launch_bounds__(64 * kWavesMax) void attn_merge_kernel(AttnArgs a)
         half8 qop[4];
         q_operand(a, qrows, j, c16, qop);
         float S[4][4];
-        chunk_scores(a.scale, opaque_neg_zero(a), L, qop, mask, j, c16, S);
+        chunk_scores(a.scale, opaque_neg_zero(a), L, qop, j, c16, S);
         const float Mnew = fmaxf(Mrun, chunk_max(S));
         const float alpha = __builtin_amdgcn_exp2f((Mrun - Mnew) * kLog2e);   // 0 for the first chunk
         float P[4][4];
