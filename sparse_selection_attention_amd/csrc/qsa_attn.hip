@@ -225,11 +225,14 @@ __device__ inline float opaque_neg_zero(const AttnArgs &a)
     return __int_as_float((int)(0x80000000u | (uint32_t)(a.n_cells >> 31)));
 }
 
-// Scaled scores of the chunk: S[b][r] is cell 16b + 4j + r, head c16. The
-// slot's penalty is the addend of the scaling fma: + -0 leaves the product as
+// Scaled scores of the chunk, kscale times the dot products: the softmax scale
+// (the records kernel, whose maxima are written), or the softmax scale times
+// log2(e) (the fused kernel, which keeps scores in log2 units so that
+// p = exp2(S - max) needs no multiply). S[b][r] is cell 16b + 4j + r, head
+// c16. The slot's penalty is the addend of the scaling fma: + -0 leaves the product as
 // it is (signed zeros included), + -inf makes an empty slot's score -inf (its
 // product is finite: the slot reads row 0 with zero scales).
-__device__ inline void chunk_scores(float scale, float nz, const WaveLds &L, const half8 (&qop)[4], int j, int c16,
+__device__ inline void chunk_scores(float kscale, float nz, const WaveLds &L, const half8 (&qop)[4], int j, int c16,
                                     float (&S)[4][4])
 {
     const floatx4 zero = {0.f, 0.f, 0.f, 0.f};
@@ -253,7 +256,7 @@ __device__ inline void chunk_scores(float scale, float nz, const WaveLds &L, con
             dot = __builtin_fmaf(acc[1][r], half_bits_to_float(kb.x >> 16), dot);
             dot = __builtin_fmaf(acc[2][r], half_bits_to_float(kb.y & 0xffffu), dot);
             dot = __builtin_fmaf(acc[3][r], half_bits_to_float(kb.y >> 16), dot);
-            S[b][r] = __builtin_fmaf(scale, dot, pen[r]);
+            S[b][r] = __builtin_fmaf(kscale, dot, pen[r]);
         }
     }
 }
@@ -270,7 +273,9 @@ __device__ inline float chunk_max(const float (&S)[4][4])
     return xor32_max(xor16_max(mx));
 }
 
-// p = exp(S - ref) for head c16, and their sum over the chunk.
+// p = exp(S - ref) for head c16, and their sum over the chunk; with kLog2Units
+// the scores are in log2 units and p = exp2(S - ref).
+template <bool kLog2Units>
 __device__ inline float chunk_probs(const float (&S)[4][4], float ref, float (&P)[4][4])
 {
     float lsum = 0.0f;
@@ -278,7 +283,7 @@ __device__ inline float chunk_probs(const float (&S)[4][4], float ref, float (&P
     for (int b = 0; b < 4; ++b)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            P[b][r] = __builtin_amdgcn_exp2f((S[b][r] - ref) * kLog2e);  // exp(0) = 1 exactly
+            P[b][r] = __builtin_amdgcn_exp2f(kLog2Units ? S[b][r] - ref : (S[b][r] - ref) * kLog2e);  // exp(0) = 1 exactly
             lsum += P[b][r];
         }
     return xor32_sum(xor16_sum(lsum));
@@ -394,7 +399,7 @@ __global__ __launch_bounds__(64) void attn_kernel(AttnArgs a)
     chunk_scores(a.scale, opaque_neg_zero(a), L, qop, j, c16, S);
     const float mx = chunk_max(S);
     float P[4][4];
-    const float lsum = chunk_probs(S, mx, P);
+    const float lsum = chunk_probs<false>(S, mx, P);
     floatx4 O[8];
 #pragma unroll
     for (int tt = 0; tt < 8; ++tt)
@@ -487,11 +492,11 @@ __global__ __launch_bounds__(64 * kWavesMax) void attn_merge_kernel(AttnArgs a)
         half8 qop[4];
         q_operand(a, qrows, j, c16, qop);
         float S[4][4];
-        chunk_scores(a.scale, opaque_neg_zero(a), L, qop, j, c16, S);
+        chunk_scores(a.scale * kLog2e, opaque_neg_zero(a), L, qop, j, c16, S);
         const float Mnew = fmaxf(Mrun, chunk_max(S));
-        const float alpha = __builtin_amdgcn_exp2f((Mrun - Mnew) * kLog2e);   // 0 for the first chunk
+        const float alpha = __builtin_amdgcn_exp2f(Mrun - Mnew);   // 0 for the first chunk
         float P[4][4];
-        Lrun = fmaf(alpha, Lrun, chunk_probs(S, Mnew, P));
+        Lrun = fmaf(alpha, Lrun, chunk_probs<true>(S, Mnew, P));
         Mrun = Mnew;
         // rescale O: every value this lane holds is of its own head c16
 #pragma unroll
@@ -546,7 +551,7 @@ __global__ __launch_bounds__(64 * kWavesMax) void attn_merge_kernel(AttnArgs a)
                 const float mv = ((const float *)Lv.ksc)[h];
                 if (mv == -INFINITY)
                     continue;
-                const float wv = __builtin_amdgcn_exp2f((mv - M) * kLog2e);
+                const float wv = __builtin_amdgcn_exp2f(mv - M);
                 Ls = fmaf(wv, ((const float *)Lv.ksc)[16 + h], Ls);
                 const float4 ov = *(const float4 *)((const float *)Lv.ktile + h * kD + 4 * ((d4 + h) & 31));
                 Os.x = fmaf(wv, ov.x, Os.x);
