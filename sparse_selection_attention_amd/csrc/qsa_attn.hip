@@ -165,14 +165,20 @@ __device__ inline uint64_t issue_chunk(const AttnArgs &a, const WaveLds &L, int3
             vs = *(const uint2 *)(a.vsc + (int64_t)sid * 4);
         }
         // K rows into the tile: instruction s writes granules 64s .. 64s+63,
-        // i.e. rows 8s .. 8s+7, eight lanes per row
+        // i.e. rows 8s .. 8s+7, eight lanes per row. All eight row ids are
+        // read first: an LDS read placed after a direct-to-LDS copy waits for
+        // it (the compiler cannot tell that they touch different LDS), which
+        // would put an LDS round trip between consecutive copies.
+        uint32_t koff[8];
 #pragma unroll
         for (int s = 0; s < 8; ++s) {
             const int row = 8 * s + (lane >> 3);
             const int lg = (lane & 7) ^ ((row >> 1) & 7);
-            const int8_t *src = a.kq + ((uint32_t)L.id[row] * kD + 16 * lg);   // n_cells * 128 < 2^32
-            __builtin_amdgcn_global_load_lds((const void *)src, (lds_void *)(L.ktile + 1024 * s), 16, 0, 0);
+            koff[s] = (uint32_t)L.id[row] * kD + 16 * lg;   // n_cells * 128 < 2^32
         }
+#pragma unroll
+        for (int s = 0; s < 8; ++s)
+            __builtin_amdgcn_global_load_lds((const void *)(a.kq + koff[s]), (lds_void *)(L.ktile + 1024 * s), 16, 0, 0);
         // V: slot s of k-step ks is cell 32ks + 16(s/4) + 4j + s%4 -- the cells
         // whose scores this lane holds -- and the lane reads dims 8*c16 .. +7
 #pragma unroll
