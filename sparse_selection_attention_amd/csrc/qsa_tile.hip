@@ -109,27 +109,23 @@ struct Raw {
     uint4 k[2];        // K: 16 bytes of each of two cells
     uint2 v[4];        // V: 8 dims of 4 consecutive cells
     uint32_t ks, vs;   // the K and V scale of one (cell, group), fp16 bits
-    uint32_t ok;       // bits 0..1: the K cells exist; 2: the scales' cell; 3..6: the V cells
 };
 
 // Issue the chunk's global reads. Every read is unconditional (cells past the
 // cache read the last cached row) so that the reads stay in flight; the cells
-// that do not exist are zeroed when the tiles are staged. Byte offsets fit 32
-// bits: n_cells * 128 < 2^32.
+// that do not exist are zeroed once the reads have landed (zero_missing). Byte
+// offsets fit 32 bits: n_cells * 128 < 2^32.
 __device__ inline void load_raw(const AttnArgs &a, int c0, int tid, Raw &R)
 {
     const int last = a.n_cells - 1;     // >= 0 whenever a chunk is walked
     const int w = tid >> 6, L = tid & 63;
-    uint32_t ok = 0;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
         const int c = c0 + 16 * w + 8 * i + (L >> 3);
-        ok |= (c <= last ? 1u : 0u) << i;
         const uint32_t cc = (uint32_t)min(c, last);
         R.k[i] = *(const uint4 *)(a.kq + (cc * kD + 16 * (L & 7)));
     }
     const int cs = c0 + 16 * w + (L >> 2);
-    ok |= (cs <= last ? 1u : 0u) << 2;
     const uint32_t ccs = (uint32_t)min(cs, last);
     R.ks = a.ksc[ccs * 4 + (L & 3)];
     R.vs = a.vsc[ccs * 4 + (L & 3)];
@@ -137,18 +133,38 @@ __device__ inline void load_raw(const AttnArgs &a, int c0, int tid, Raw &R)
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
         const int c = c0 + v_cell0(pq) + s;
-        ok |= (c <= last ? 1u : 0u) << (3 + s);
         const uint32_t cc = (uint32_t)min(c, last);
         R.v[s] = *(const uint2 *)(a.vq + (cc * kD + 8 * db));
     }
-    R.ok = ok;
+}
+
+// Zero what load_raw read for cells at or past n_cells (it read the last
+// cached row in their place): codes and scales, so that such a cell adds
+// nothing to the tiles, the scores' weights or the V-scale exponents.
+__device__ inline void zero_missing(Raw &R, int c0, int n_cells, int tid)
+{
+    const int w = tid >> 6, L = tid & 63;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+        if (c0 + 16 * w + 8 * i + (L >> 3) >= n_cells)
+            R.k[i] = make_uint4(0u, 0u, 0u, 0u);
+    if (c0 + 16 * w + (L >> 2) >= n_cells) {
+        R.ks = 0u;
+        R.vs = 0u;
+    }
+    const int pq = tid & 15;
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+        if (c0 + v_cell0(pq) + s >= n_cells)
+            R.v[s] = make_uint2(0u, 0u);
 }
 
 // Largest biased exponent of this thread's V scale over the lanes of the wave
-// that hold the same scale group (lane % 4); 0 for a cell that does not exist.
+// that hold the same scale group (lane % 4); a cell that does not exist has a
+// zero scale (zero_missing), of exponent 0.
 __device__ inline int group_max_exponent(const Raw &R)
 {
-    int e = ((R.ok >> 2) & 1u) ? (int)((R.vs >> 10) & 31u) : 0;
+    int e = (int)((R.vs >> 10) & 31u);
     // lanes l, l + 4, l + 8, l + 12 of a row: two row rotations (by 4, then 8)
     e = max(e, __builtin_amdgcn_update_dpp(0, e, 0x124, 0xf, 0xf, false));   // row_ror:4
     e = max(e, __builtin_amdgcn_update_dpp(0, e, 0x128, 0xf, 0xf, false));   // row_ror:8
@@ -175,22 +191,18 @@ __device__ inline void stage_tiles(uint8_t *lds, int tid, const Raw &R, const in
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
         const int c = 16 * w + 8 * i + (L >> 3);
-        const uint4 kr = ((R.ok >> i) & 1u) ? R.k[i] : make_uint4(0u, 0u, 0u, 0u);
+        const uint4 kr = R.k[i];
         *(half8 *)(lds + tk_offset(c, 2 * (L & 7))) = i8x8_to_half8(make_uint2(kr.x, kr.y));
         *(half8 *)(lds + tk_offset(c, 2 * (L & 7) + 1)) = i8x8_to_half8(make_uint2(kr.z, kr.w));
     }
     // the (cell, group) scales: K as read, V times 2^kg at the cell's position
     const int cs = 16 * w + (L >> 2), g = L & 3;
-    const bool oks = ((R.ok >> 2) & 1u) != 0;
-    *(uint16_t *)(lds + kLKs + cs * 8 + 2 * g) = oks ? (uint16_t)R.ks : (uint16_t)0;
+    *(uint16_t *)(lds + kLKs + cs * 8 + 2 * g) = (uint16_t)R.ks;
     const int kgs = g == 0 ? kg[0] : g == 1 ? kg[1] : g == 2 ? kg[2] : kg[3];
     const _Float16 vsn = (_Float16)(half_bits_to_float(R.vs) * pow2i(kgs));
-    *(_Float16 *)(lds + kLVs + g * kVsRow + 2 * cell_pos(cs)) = oks ? vsn : (_Float16)0.0f;
+    *(_Float16 *)(lds + kLVs + g * kVsRow + 2 * cell_pos(cs)) = vsn;
     // V: dims 8db .. +7 of positions 4pq .. +3 as fp16 codes (exact), transposed
-    uint2 v[4];
-#pragma unroll
-    for (int s = 0; s < 4; ++s)
-        v[s] = ((R.ok >> (3 + s)) & 1u) ? R.v[s] : make_uint2(0u, 0u);
+    const uint2 (&v)[4] = R.v;
     const I8Scale cv = i8_scale(0);
     const int db = tid >> 4, pq = tid & 15;
     const int gp = pq >> 1, half = 8 * (pq & 1);
@@ -339,6 +351,8 @@ __global__ __launch_bounds__(kTileThreads * G) void attn_tile_kernel(AttnArgs a,
         // here so that the contractions below wait on none of the next
         // chunk's reads, which are issued before them
         __builtin_amdgcn_s_waitcnt(0);
+        if (act && c0 + kChunk > a.n_cells)     // uniform: only a chunk that reaches past the cache
+            zero_missing(R, c0, a.n_cells, tid);
         if (act) {
             const int eg = group_max_exponent(R);
             if (lane < 4)
