@@ -71,6 +71,9 @@ constexpr int attn_lds_bytes(int nw, int H, bool gated) { return nw * kWaveBytes
 
 typedef __attribute__((address_space(3))) void lds_void;
 
+// cache-policy operand of the buffer store builtins: the nontemporal bit
+constexpr int kCachePolicyNT = 2;
+
 // K tile: row r (a cell of the chunk) holds 8 granules of 16 bytes; logical
 // granule lg sits at physical granule lg ^ ((r >> 1) & 7). Rows of equal parity
 // then spread over all eight granule positions, so the sixteen rows read by one
@@ -419,13 +422,31 @@ __global__ __launch_bounds__(64) void attn_kernel(AttnArgs a)
         for (int tt = 0; tt < 8; ++tt)
             O[tt] *= down;
     }
+    if ((int)(blockIdx.x >> 3) < a.nt_per_xcd) {
+        // early in this XCD's walk: nontemporal stores, through a buffer
+        // resource over this record's H head rows (raw 32-bit elements:
+        // DATA_FORMAT 32 in the descriptor's last word, no stride, no swizzle)
+        const __amdgpu_buffer_rsrc_t rs =
+            __builtin_amdgcn_make_buffer_rsrc(a.o + rec * kD, 0, a.H * kD * (int)sizeof(float), 0x00020000);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const int head = 4 * j + r;
-        if (head < a.H) {
-            float *dst = a.o + (rec + head) * kD + 8 * c16;
-            *(float4 *)dst = make_float4(O[0][r], O[1][r], O[2][r], O[3][r]);
-            *(float4 *)(dst + 4) = make_float4(O[4][r], O[5][r], O[6][r], O[7][r]);
+        for (int r = 0; r < 4; ++r) {
+            const int head = 4 * j + r;
+            if (head < a.H) {
+                const int off = (head * kD + 8 * c16) * (int)sizeof(float);
+                const floatx4 v0 = {O[0][r], O[1][r], O[2][r], O[3][r]}, v1 = {O[4][r], O[5][r], O[6][r], O[7][r]};
+                __builtin_amdgcn_raw_buffer_store_b128(v0, rs, off, 0, kCachePolicyNT);
+                __builtin_amdgcn_raw_buffer_store_b128(v1, rs, off + 16, 0, kCachePolicyNT);
+            }
+        }
+    } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int head = 4 * j + r;
+            if (head < a.H) {
+                float *dst = a.o + (rec + head) * kD + 8 * c16;
+                *(float4 *)dst = make_float4(O[0][r], O[1][r], O[2][r], O[3][r]);
+                *(float4 *)(dst + 4) = make_float4(O[4][r], O[5][r], O[6][r], O[7][r]);
+            }
         }
     }
     if (j == 0 && c16 < a.H) {
