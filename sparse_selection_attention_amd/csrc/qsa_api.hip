@@ -7,7 +7,6 @@
 #include "qsa.h"
 #include "qsa_internal.h"
 
-#include <algorithm>
 #include <atomic>
 #include <cstdarg>
 #include <cstdio>
@@ -195,14 +194,7 @@ qsa_status qsa_attn(const void *q, const int8_t *kq, const int8_t *vq,
     a.l = reinterpret_cast<float *>(pb + l_off);
     a.n_blocks = (int32_t)n_blocks;
     a.blocks_per_xcd = (int32_t)per_xcd;
-    {
-        // each XCD walks its range in order: the last kCachedRecordBytes of
-        // records (spread evenly over the XCDs) are written cached, the rest
-        // nontemporal
-        const int64_t rec_bytes = (int64_t)T * a.C * H * D * (int64_t)sizeof(float);
-        const int64_t cached = std::min<int64_t>(rec_bytes, qsa::kCachedRecordBytes);
-        a.nt_per_xcd = (int32_t)(per_xcd - (per_xcd * cached + rec_bytes - 1) / rec_bytes);
-    }
+    a.nt_records = (int64_t)T * a.C * H * D * (int64_t)sizeof(float) > qsa::kNontemporalRecordBytes;
     if (!ids)   // implicit rows: blocks of (token, head) rows share each chunk's cells
         return launched(qsa::launch_attn_tile(a, static_cast<hipStream_t>(stream)), "qsa_attn");
     return launched(qsa::launch_attn(a, static_cast<hipStream_t>(stream)), "qsa_attn");

@@ -49,7 +49,9 @@
 //     exponent and one packed subtraction, all visible to the compiler.
 // Record waves are ordered by chunk first (all tokens of chunk 0, then chunk
 // 1, ...) and each XCD walks a contiguous range of them, so the cells one XCD
-// gathers stay within a narrow band of the cache, served from its L2.
+// gathers stay within a narrow band of the cache, served from its L2. A record
+// is written in whole 1 KB runs, nontemporal when the call's records are too
+// large to stay cached until the merge, so that they do not evict that band.
 #include "qsa_internal.h"
 #include "qsa_device.h"
 
@@ -422,32 +424,35 @@ __global__ __launch_bounds__(64) void attn_kernel(AttnArgs a)
         for (int tt = 0; tt < 8; ++tt)
             O[tt] *= down;
     }
-    if ((int)(blockIdx.x >> 3) < a.nt_per_xcd) {
-        // early in this XCD's walk: nontemporal stores, through a buffer
-        // resource over this record's H head rows (raw 32-bit elements:
-        // DATA_FORMAT 32 in the descriptor's last word, no stride, no swizzle)
-        const __amdgpu_buffer_rsrc_t rs =
-            __builtin_amdgcn_make_buffer_rsrc(a.o + rec * kD, 0, a.H * kD * (int)sizeof(float), 0x00020000);
+    // The record leaves in whole 1 KB runs: its H head rows (512 B each, in
+    // memory order) are laid out in the K tile, free since the scores, and
+    // each store instruction then writes 1 KB of consecutive bytes (the MFMA
+    // layout would have each instruction fill half of each of 16 lines). The
+    // stores go through a buffer resource over the record (raw 32-bit
+    // elements: DATA_FORMAT 32 in the descriptor's last word, no stride, no
+    // swizzle), which also drops the second half of the last run when H is odd.
+    float *st = (float *)L.ktile;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int head = 4 * j + r;
-            if (head < a.H) {
-                const int off = (head * kD + 8 * c16) * (int)sizeof(float);
-                const floatx4 v0 = {O[0][r], O[1][r], O[2][r], O[3][r]}, v1 = {O[4][r], O[5][r], O[6][r], O[7][r]};
-                __builtin_amdgcn_raw_buffer_store_b128(v0, rs, off, 0, kCachePolicyNT);
-                __builtin_amdgcn_raw_buffer_store_b128(v1, rs, off + 16, 0, kCachePolicyNT);
-            }
+    for (int r = 0; r < 4; ++r) {
+        const int head = 4 * j + r;
+        if (head < a.H) {
+            float *row = st + head * kD + 8 * c16;
+            *(float4 *)row = make_float4(O[0][r], O[1][r], O[2][r], O[3][r]);
+            *(float4 *)(row + 4) = make_float4(O[4][r], O[5][r], O[6][r], O[7][r]);
         }
+    }
+    wave_sync_lds();
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc(a.o + rec * kD, 0, a.H * kD * (int)sizeof(float), 0x00020000);
+    const int runs = (a.H + 1) / 2;
+    if (a.nt_records) {              // uniform
+        for (int i = 0; i < runs; ++i)
+            __builtin_amdgcn_raw_buffer_store_b128(*(const floatx4 *)(st + 4 * (64 * i + lane)), rs,
+                                                   16 * (64 * i + lane), 0, kCachePolicyNT);
     } else {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int head = 4 * j + r;
-            if (head < a.H) {
-                float *dst = a.o + (rec + head) * kD + 8 * c16;
-                *(float4 *)dst = make_float4(O[0][r], O[1][r], O[2][r], O[3][r]);
-                *(float4 *)(dst + 4) = make_float4(O[4][r], O[5][r], O[6][r], O[7][r]);
-            }
-        }
+        for (int i = 0; i < runs; ++i)
+            __builtin_amdgcn_raw_buffer_store_b128(*(const floatx4 *)(st + 4 * (64 * i + lane)), rs,
+                                                   16 * (64 * i + lane), 0, 0);
     }
     if (j == 0 && c16 < a.H) {
         a.m[rec + c16] = mx;

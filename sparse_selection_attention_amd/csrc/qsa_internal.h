@@ -32,16 +32,16 @@ struct AttnArgs {
     float *sums;              // [T][H][D/16] per-16 sums of out, or nullptr
     int32_t n_blocks;         // workgroups that carry work: C x T one-wave records, T fused
     int32_t blocks_per_xcd;   // workgroups each XCD walks through
-    int32_t nt_per_xcd;       // records kernel: the first nt_per_xcd workgroups of each XCD's walk
-                              // store their records nontemporal
+    int32_t nt_records;       // records kernel: store the chunk records nontemporal
 };
 
-// Chunk records written in the last part of a qsa_attn launch, up to this many
-// bytes, are stored as ordinary (cached) stores, so that most of them are still
-// in the Infinity Cache (256 MB on MI355X) when qsa_merge reads them; records
-// written before that are stored nontemporal, so that they do not push the
-// cache rows the gathers reuse out of L2 and the Infinity Cache.
-constexpr int64_t kCachedRecordBytes = int64_t(160) << 20;
+// A qsa_attn call whose chunk records take more than this many bytes stores
+// them nontemporal. Such records cannot stay in the Infinity Cache (256 MB on
+// MI355X) until qsa_merge reads them anyway, and streaming them past L2 and
+// the Infinity Cache leaves both to the cache rows the gathers reuse. Smaller
+// calls (decode windows, short prompts) keep their records in the caches for
+// the merge.
+constexpr int64_t kNontemporalRecordBytes = int64_t(128) << 20;
 
 struct MergeArgs {
     const float *o, *m, *l;
