@@ -265,6 +265,48 @@ def test_run_to_run_determinism():
         assert np.array_equal(x.view(np.uint8), y.view(np.uint8))
 
 
+@pytest.mark.parametrize("H,T", [(12, 700), (5, 1700)])
+def test_large_call_records_match_small_calls(H, T):
+    """A call whose records exceed 128 MB stores them nontemporal; a small call
+    stores them cached. Both write each record in whole 1 KB runs. The records
+    and outputs of the tokens a small call covers must be bitwise equal to the
+    large call's (a token's records depend on its own row only). H = 5 leaves
+    half of each record's last run unused."""
+    pos0, K, D = 30000, 2051, 128
+    L = synth.make_layer(7, 0, T, H, pos0 + T)
+    ids = synth.evenly_spaced_ids(pos0, T, K)
+    C = ids.shape[1] // 64
+    assert T * C * H * D * 4 > (128 << 20)
+    q, kq, vq, ksc, vsc = (to_dev(x) for x in (L.q, L.kq, L.vq, L.ksc, L.vsc))
+    ids_d = to_dev(ids)
+    scale = float(synth.SCALE_1_SQRT_128)
+    big = qsa.alloc_part(T, H, D, C)
+    big.fill_(0xFF)
+    out_big = torch.empty(T, H, D, dtype=torch.float16, device=dev())
+    qsa.qsa_attn(q, kq, vq, ksc, vsc, ids_d, pos0, scale, big)
+    qsa.qsa_merge(big, C, out_big)
+    ob, mb, lb = qsa.part_views(big, T, H, D, C)
+    for t0 in (0, T // 2 - 37, T - 64):
+        n = 64
+        small = qsa.alloc_part(n, H, D, C)
+        small.fill_(0xFF)
+        out_s = torch.empty(n, H, D, dtype=torch.float16, device=dev())
+        qsa.qsa_attn(q[t0:t0 + n], kq, vq, ksc, vsc, ids_d[t0:t0 + n], pos0 + t0, scale, small)
+        qsa.qsa_merge(small, C, out_s)
+        os_, ms, ls = qsa.part_views(small, n, H, D, C)
+        torch.cuda.synchronize()
+        _print("large vs small call: H=%d T=%d tokens %d..%d" % (H, T, t0, t0 + n - 1))
+        assert torch.equal(ms.view(torch.int32), mb[t0:t0 + n].view(torch.int32))
+        assert torch.equal(ls.view(torch.int32), lb[t0:t0 + n].view(torch.int32))
+        written = torch.isfinite(ms)
+        assert torch.equal(os_[written].view(torch.int32), ob[t0:t0 + n][written].view(torch.int32))
+        assert torch.equal(out_s.view(torch.int16), out_big[t0:t0 + n].view(torch.int16))
+    # and the large call against the oracle on a few tokens
+    for t in (0, T // 3, T - 1):
+        r = oracle_token(L, ids, pos0, synth.SCALE_1_SQRT_128, t)
+        check_out(out_big[t].cpu().numpy(), r["out64"], "large call H=%d t=%d" % (H, t))
+
+
 def test_probe_case_vs_oracle_all_tokens():
     L, ids, pos0 = probe_case(seed=6)
     out, o, m, l, C = run_attn(L, ids, pos0, synth.SCALE_1_SQRT_128)
