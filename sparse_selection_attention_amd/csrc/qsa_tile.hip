@@ -279,16 +279,56 @@ __device__ inline void pv_accumulate(const uint8_t *lds, const float (&P)[4][4],
     }
 }
 
+// Synchronisation of the four waves of one group. With one group per
+// workgroup it is the workgroup barrier. With several, a workgroup barrier
+// would also hold each group for the others, which walk other chunks, so the
+// waves of a group meet on a counter in LDS instead: each wave adds one to it
+// and waits until the group's four additions of this round are in. The
+// counter only grows, and each wave compares it with its own running target.
+// The wait is bounded (kBarrierSpins polls, far longer than any chunk takes),
+// so every wave always leaves it.
+constexpr int kBarrierSpins = 1 << 16;
+
+template <int G>
+__device__ inline void group_sync(int *ctr, int &target)
+{
+    if constexpr (G == 1) {
+        __syncthreads();
+    } else {
+        target += kTileThreads / 64;
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");   // this wave's LDS writes are done
+        if ((threadIdx.x & 63) == 0)
+            __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+#pragma unroll 1
+        for (int spin = 0; spin < kBarrierSpins; ++spin) {
+            const int seen = __builtin_amdgcn_readfirstlane(
+                __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP));
+            if (seen >= target)
+                break;
+            __builtin_amdgcn_s_sleep(1);
+        }
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");   // the group's writes are visible
+    }
+}
+
 // G groups of four waves share a workgroup's rows: group gi walks chunks
 // k_lo + gi, k_lo + gi + G, ... with LDS tiles of its own, and the groups'
 // running (max, denominator, output) are combined at the end (fused kernel).
 template <bool kFused, int G>
 __global__ __launch_bounds__(kTileThreads * G) void attn_tile_kernel(AttnArgs a, int n_parts)
 {
-    __shared__ __align__(16) uint8_t lds_all[G * kTileLds];
-    const int gi = (int)threadIdx.x / kTileThreads;
+    __shared__ __align__(16) uint8_t lds_all[G * kTileLds + (G > 1 ? 16 : 0)];
+    const int gi = G == 1 ? (int)threadIdx.x / kTileThreads
+                          : __builtin_amdgcn_readfirstlane((int)threadIdx.x / kTileThreads);   // uniform per wave
     uint8_t *lds = lds_all + gi * kTileLds;
     int *s_e = (int *)(lds + kLE);
+    int *s_bar = (int *)(lds_all + G * kTileLds) + gi;   // this group's barrier counter (G > 1)
+    int bar_target = 0;
+    if constexpr (G > 1) {
+        if (threadIdx.x < G)
+            ((int *)(lds_all + G * kTileLds))[threadIdx.x] = 0;
+        __syncthreads();
+    }
 
     const int tid = (int)threadIdx.x % kTileThreads;    // thread within the group
     const int lane = tid & 63, w = tid >> 6;
@@ -358,14 +398,14 @@ __global__ __launch_bounds__(kTileThreads * G) void attn_tile_kernel(AttnArgs a,
             if (lane < 4)
                 s_e[4 * w + lane] = eg;         // lane l holds scale group l
         }
-        __syncthreads();                        // the previous chunk's tiles are no longer read
+        group_sync<G>(s_bar, bar_target);       // the previous chunk's tiles are no longer read
         int kg[4];
 #pragma unroll
         for (int g = 0; g < 4; ++g)
             kg[g] = group_shift(max(max(s_e[g], s_e[4 + g]), max(s_e[8 + g], s_e[12 + g])));
         if (act)
             stage_tiles(lds, tid, R, kg);
-        __syncthreads();                        // the chunk's tiles are in place
+        group_sync<G>(s_bar, bar_target);       // the chunk's tiles are in place
         if (!act)
             continue;
         if (k + G <= k_end)
