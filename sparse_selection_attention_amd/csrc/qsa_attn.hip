@@ -530,10 +530,14 @@ __global__ __launch_bounds__(64 * kWavesMax) void attn_merge_kernel(AttnArgs a)
         float P[4][4];
         Lrun = fmaf(alpha, Lrun, chunk_probs<true>(S, Mnew, P));
         Mrun = Mnew;
-        // rescale O: every value this lane holds is of its own head c16
+        // rescale O: every value this lane holds is of its own head c16; a
+        // chunk that moves no head's running max (alpha = 1 in every lane)
+        // leaves O as it is
+        if (__ballot(alpha != 1.0f) != 0) {     // uniform
 #pragma unroll
-        for (int tt = 0; tt < 8; ++tt)
-            O[tt] *= alpha;
+            for (int tt = 0; tt < 8; ++tt)
+                O[tt] *= alpha;
+        }
         if (kr != 0) {              // the chunk's V codes carry 2^-k: put 2^k on p
             const float down = pow2f(kr);
 #pragma unroll
