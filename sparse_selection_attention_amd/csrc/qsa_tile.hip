@@ -285,8 +285,9 @@ __device__ inline void pv_accumulate(const uint8_t *lds, const float (&P)[4][4],
 // waves of a group meet on a counter in LDS instead: each wave adds one to it
 // and waits until the group's four additions of this round are in. The
 // counter only grows, and each wave compares it with its own running target.
-// The wait is bounded (kBarrierSpins polls, far longer than any chunk takes),
-// so every wave always leaves it.
+// The wait polls the counter with LDS reads (a sleep between polls made the
+// kernel 2% slower) and is bounded (kBarrierSpins polls, far longer than any
+// chunk takes), so every wave always leaves it.
 constexpr int kBarrierSpins = 1 << 16;
 
 template <int G>
@@ -305,7 +306,6 @@ __device__ inline void group_sync(int *ctr, int &target)
                 __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP));
             if (seen >= target)
                 break;
-            __builtin_amdgcn_s_sleep(1);
         }
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");   // the group's writes are visible
     }
