@@ -197,6 +197,53 @@ __device__ inline uint64_t issue_chunk(const AttnArgs &a, const WaveLds &L, int3
     return mask;
 }
 
+// The two halves of issue_chunk, for a wave that issues the next chunk's
+// reads while it still computes the current one. issue_k publishes the ids and
+// penalties, reads the scales and copies the K rows into the tile (the tile
+// must no longer be read); issue_v reads the V rows of the ids issue_k
+// published into the PV operand registers (which must no longer be read).
+__device__ inline uint64_t issue_k(const AttnArgs &a, const WaveLds &L, int32_t id, int lane, uint2 &ks, uint2 &vs)
+{
+    const bool valid = (uint32_t)id < (uint32_t)a.n_cells;
+    const int32_t sid = valid ? id : 0;
+    const uint64_t mask = __ballot(valid);
+    L.id[lane] = sid;
+    L.pen[lane] = valid ? -0.0f : -INFINITY;
+    wave_sync_lds();
+    ks = make_uint2(0u, 0u);
+    vs = make_uint2(0u, 0u);
+    if (mask != 0) {
+        if (valid) {
+            ks = *(const uint2 *)(a.ksc + (int64_t)sid * 4);
+            vs = *(const uint2 *)(a.vsc + (int64_t)sid * 4);
+        }
+        uint32_t koff[8];                        // all ids first, as in issue_chunk
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+            const int row = 8 * s + (lane >> 3);
+            const int lg = (lane & 7) ^ ((row >> 1) & 7);
+            koff[s] = (uint32_t)L.id[row] * kD + 16 * lg;
+        }
+#pragma unroll
+        for (int s = 0; s < 8; ++s)
+            __builtin_amdgcn_global_load_lds((const void *)(a.kq + koff[s]), (lds_void *)(L.ktile + 1024 * s), 16, 0, 0);
+    }
+    return mask;
+}
+
+__device__ inline void issue_v(const AttnArgs &a, const WaveLds &L, uint64_t mask, int j, int c16, uint2 (&vraw)[2][8])
+{
+    if (mask != 0) {
+#pragma unroll
+        for (int ks2 = 0; ks2 < 2; ++ks2)
+#pragma unroll
+            for (int s = 0; s < 8; ++s) {
+                const int cell = 32 * ks2 + 16 * (s >> 2) + 4 * j + (s & 3);
+                vraw[ks2][s] = *(const uint2 *)(a.vq + ((uint32_t)L.id[cell] * kD + 8 * c16));
+            }
+    }
+}
+
 // Publish the chunk's scales to LDS. When vq * vsc could leave fp16 range (the
 // chunk's largest V scale reaches 2^9), the V codes are converted as
 // vq * 2^-k, k = e - 23 (e the largest biased V-scale exponent, so k <= 7),
@@ -476,6 +523,7 @@ __global__ __launch_bounds__(64) void attn_kernel(AttnArgs a)
 // "preflight / ownership": the fused kernel keeps the sigmoid gate and the
 // per-16 sums).
 
+template <bool kPipelined>
 __global__ __launch_bounds__(64 * kWavesMax) void attn_merge_kernel(AttnArgs a)
 {
     extern __shared__ __align__(16) uint8_t lds[];
@@ -503,51 +551,116 @@ __global__ __launch_bounds__(64 * kWavesMax) void attn_merge_kernel(AttnArgs a)
     for (int tt = 0; tt < 8; ++tt)
         O[tt] = (floatx4){0.f, 0.f, 0.f, 0.f};
 
-    // each chunk's slot ids are read one chunk ahead (the last chunk re-reads
-    // its own), so a chunk's gathers start without a round trip for its ids
-    int32_t id_next = slot_id(a, t, min(w, a.C - 1), lane0);
-    for (int k = w; k < a.C; k += nw) {
-        // lane-derived offsets are rebuilt every chunk (cheap VALU) rather than
-        // hoisted out of the loop, where they would pin registers throughout
-        int lane = lane0;
-        asm volatile("" : "+v"(lane));
-        const int j = lane >> 4, c16 = lane & 15;
-        uint2 ks, vs;
+    if constexpr (kPipelined) {
+        // waves that walk several chunks issue the next chunk's reads while
+        // they compute the current one: its ids, scales and K rows as soon as
+        // the scores have been taken from the K tile, its V rows once the
+        // products have read the current ones. The arithmetic is the one below.
+        uint2 ks = make_uint2(0u, 0u), vs = make_uint2(0u, 0u);
         uint2 vraw[2][8];
-        const uint64_t mask = issue_chunk(a, L, id_next, lane, j, c16, ks, vs, vraw);
-        __builtin_amdgcn_s_waitcnt(0);           // the K tile copy has landed
-        wave_sync_lds();
-        id_next = slot_id(a, t, min(k + nw, a.C - 1), lane);   // in flight during this chunk
-        if (mask == 0)
-            continue;                            // uniform: an empty chunk adds nothing
-        const int kr = stage_scales(L, lane, ks, vs);
-        half8 qop[4];
-        q_operand(a, qrows, j, c16, qop);
-        float S[4][4];
-        chunk_scores(a.scale * kLog2e, opaque_neg_zero(a), L, qop, j, c16, S);
-        const float Mnew = fmaxf(Mrun, chunk_max(S));
-        const float alpha = __builtin_amdgcn_exp2f(Mrun - Mnew);   // 0 for the first chunk
-        float P[4][4];
-        Lrun = fmaf(alpha, Lrun, chunk_probs<true>(S, Mnew, P));
-        Mrun = Mnew;
-        // rescale O: every value this lane holds is of its own head c16; a
-        // chunk that moves no head's running max (alpha = 1 in every lane)
-        // leaves O as it is
-        if (__ballot(alpha != 1.0f) != 0) {     // uniform
-#pragma unroll
-            for (int tt = 0; tt < 8; ++tt)
-                O[tt] *= alpha;
+        uint64_t mask = 0;
+        if (w < a.C) {
+            int lane = lane0;
+            asm volatile("" : "+v"(lane));
+            mask = issue_k(a, L, slot_id(a, t, w, lane), lane, ks, vs);
+            issue_v(a, L, mask, lane >> 4, lane & 15, vraw);
         }
-        if (kr != 0) {              // the chunk's V codes carry 2^-k: put 2^k on p
-            const float down = pow2f(kr);
+        int32_t id_next = slot_id(a, t, min(w + nw, a.C - 1), lane0);
+        for (int k = w; k < a.C; k += nw) {
+            int lane = lane0;
+            asm volatile("" : "+v"(lane));
+            const int j = lane >> 4, c16 = lane & 15;
+            __builtin_amdgcn_s_waitcnt(0);       // this chunk's tile, rows and scales; the next chunk's ids
+            wave_sync_lds();
+            const bool more = k + nw < a.C;      // uniform
+            const bool live = mask != 0;         // uniform: an empty chunk adds nothing
+            float P[4][4];
+            float alpha = 1.0f;
+            int kr = 0;
+            if (live) {
+                kr = stage_scales(L, lane, ks, vs);
+                half8 qop[4];
+                q_operand(a, qrows, j, c16, qop);
+                float S[4][4];
+                chunk_scores(a.scale * kLog2e, opaque_neg_zero(a), L, qop, j, c16, S);
+                const float Mnew = fmaxf(Mrun, chunk_max(S));
+                alpha = __builtin_amdgcn_exp2f(Mrun - Mnew);   // 0 for the first chunk
+                Lrun = fmaf(alpha, Lrun, chunk_probs<true>(S, Mnew, P));
+                Mrun = Mnew;
+            }
+            uint64_t mask_n = 0;
+            if (more)
+                mask_n = issue_k(a, L, id_next, lane, ks, vs);
+            if (live) {
+                if (__ballot(alpha != 1.0f) != 0) {     // uniform
 #pragma unroll
-            for (int b = 0; b < 4; ++b)
+                    for (int tt = 0; tt < 8; ++tt)
+                        O[tt] *= alpha;
+                }
+                if (kr != 0) {
+                    const float down = pow2f(kr);
 #pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    P[b][r] *= down;
+                    for (int b = 0; b < 4; ++b)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r)
+                            P[b][r] *= down;
+                }
+                pv_accumulate<true>(P, vraw, L, j, c16, kr, O);
+            }
+            if (more) {
+                issue_v(a, L, mask_n, j, c16, vraw);
+                id_next = slot_id(a, t, min(k + 2 * nw, a.C - 1), lane);
+            }
+            mask = mask_n;
+            wave_sync_lds();
         }
-        pv_accumulate<true>(P, vraw, L, j, c16, kr, O);
-        wave_sync_lds();                         // the tile is rewritten by the next chunk
+    } else {
+        // each chunk's slot ids are read one chunk ahead (the last chunk re-reads
+        // its own), so a chunk's gathers start without a round trip for its ids
+        int32_t id_next = slot_id(a, t, min(w, a.C - 1), lane0);
+        for (int k = w; k < a.C; k += nw) {
+            // lane-derived offsets are rebuilt every chunk (cheap VALU) rather than
+            // hoisted out of the loop, where they would pin registers throughout
+            int lane = lane0;
+            asm volatile("" : "+v"(lane));
+            const int j = lane >> 4, c16 = lane & 15;
+            uint2 ks, vs;
+            uint2 vraw[2][8];
+            const uint64_t mask = issue_chunk(a, L, id_next, lane, j, c16, ks, vs, vraw);
+            __builtin_amdgcn_s_waitcnt(0);           // the K tile copy has landed
+            wave_sync_lds();
+            id_next = slot_id(a, t, min(k + nw, a.C - 1), lane);   // in flight during this chunk
+            if (mask == 0)
+                continue;                            // uniform: an empty chunk adds nothing
+            const int kr = stage_scales(L, lane, ks, vs);
+            half8 qop[4];
+            q_operand(a, qrows, j, c16, qop);
+            float S[4][4];
+            chunk_scores(a.scale * kLog2e, opaque_neg_zero(a), L, qop, j, c16, S);
+            const float Mnew = fmaxf(Mrun, chunk_max(S));
+            const float alpha = __builtin_amdgcn_exp2f(Mrun - Mnew);   // 0 for the first chunk
+            float P[4][4];
+            Lrun = fmaf(alpha, Lrun, chunk_probs<true>(S, Mnew, P));
+            Mrun = Mnew;
+            // rescale O: every value this lane holds is of its own head c16; a
+            // chunk that moves no head's running max (alpha = 1 in every lane)
+            // leaves O as it is
+            if (__ballot(alpha != 1.0f) != 0) {     // uniform
+#pragma unroll
+                for (int tt = 0; tt < 8; ++tt)
+                    O[tt] *= alpha;
+            }
+            if (kr != 0) {              // the chunk's V codes carry 2^-k: put 2^k on p
+                const float down = pow2f(kr);
+#pragma unroll
+                for (int b = 0; b < 4; ++b)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        P[b][r] *= down;
+            }
+            pv_accumulate<true>(P, vraw, L, j, c16, kr, O);
+            wave_sync_lds();                         // the tile is rewritten by the next chunk
+        }
     }
 
     // ---- combine the waves: (M, L) and O through LDS, then divide once ---
@@ -632,7 +745,12 @@ hipError_t launch_attn_merge(const AttnArgs &a, hipStream_t stream)
     // serial walk over the chunks (2051 cells at T = 1: 33.8 -> 26.4 us)
     const int nw = a.C <= kWavesMax ? a.C : (a.T <= 64 ? kWavesMax : kWaves);
     dim3 grid(8 * a.blocks_per_xcd), block(64 * nw);
-    hipLaunchKernelGGL(attn_merge_kernel, grid, block, attn_lds_bytes(nw, a.H, a.gate != nullptr), stream, a);
+    // rows longer than one chunk per wave take the pipelined walk; a decode
+    // window (one chunk per wave) has nothing to overlap
+    if (a.C > nw)
+        hipLaunchKernelGGL(attn_merge_kernel<true>, grid, block, attn_lds_bytes(nw, a.H, a.gate != nullptr), stream, a);
+    else
+        hipLaunchKernelGGL(attn_merge_kernel<false>, grid, block, attn_lds_bytes(nw, a.H, a.gate != nullptr), stream, a);
     return hipGetLastError();
 }
 
