@@ -71,6 +71,27 @@ def test_fused_probe_case_all_tokens():
     assert np.all(out[7].view(np.uint16) == 0)    # the row with no valid slot is +0
 
 
+@pytest.mark.parametrize("T", [150, 40])          # 4 waves (5 chunks each) and 8 waves (2 or 3 each)
+def test_fused_walk_over_empty_chunks(T):
+    """Rows of 20 chunks, so each wave walks several and issues the next
+    chunk's reads during the current one. Whole chunks are empty at the start
+    of a wave's walk, in the middle, several in a row, and at the end; one row
+    has no valid slot and another a single one. Every token against the oracle."""
+    L, ids, pos0 = probe_case(T=T, C=20, n_cells=2000, seed=17, p_poison=0.2)
+    for c in (0, 5, 6, 7, 13, 19):               # empty chunks in every row
+        ids[:, 64 * c: 64 * c + 64] = -1
+    ids[11, :] = -1                              # a row with no valid slot
+    ids[12, :] = -1
+    ids[12, 64 * 9 + 3] = 77                     # a row with one cell
+    out = run_fused(L, ids, pos0, synth.SCALE_1_SQRT_128)
+    refs = oracle_tokens(L, ids, pos0, synth.SCALE_1_SQRT_128, list(range(T)))
+    for t, r in refs.items():
+        check_out(out[t], r["out64"], "fused empty-chunk walk T=%d t=%d" % (T, t))
+    assert np.all(out[11].view(np.uint16) == 0)
+    rec = run_attn(L, ids, pos0, synth.SCALE_1_SQRT_128)[0]
+    assert np.abs(rec.astype(np.float64) - out.astype(np.float64)).max() <= 2e-4
+
+
 def test_fused_one_cell_selection_is_bitwise():
     T, H, n_cells = 64, 12, 300
     L = synth.make_layer(4, 0, T, H, n_cells)
