@@ -79,14 +79,15 @@ def _check(out, refs, toks, hide_big, what):
 
 
 @pytest.mark.parametrize("hide_big", [True, False])
-def test_explicit_ids_records_and_fused(hide_big):
-    T, H, pos0 = 24, 12, 900
+@pytest.mark.parametrize("nc,pos0", [(5, 900), (20, 2000)])   # one chunk per wave; several (pipelined fused walk)
+def test_explicit_ids_records_and_fused(hide_big, nc, pos0):
+    T, H = 24, 12
     L = mixed_layer(T, H, pos0, 41, hide_big)
     rng = np.random.default_rng(2)
-    ids = np.full((T, 5 * 64), -1, np.int32)
+    ids = np.full((T, nc * 64), -1, np.int32)
     for t in range(T):
         p = pos0 + t
-        width = int(rng.integers(40, 5 * 64))
+        width = int(rng.integers(40, nc * 64))
         ids[t, :width] = np.sort(rng.choice(p + 1, width, replace=False))
     scale = synth.SCALE_1_SQRT_128
     out, o, m, l, C = run_attn(L, ids, pos0, scale)
