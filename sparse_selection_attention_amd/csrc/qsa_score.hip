@@ -119,17 +119,30 @@ __device__ inline void stage_k(uint8_t *buf, const floatx4 (&kreg)[4], int tid)
     }
 }
 
-__global__ __launch_bounds__(kScoreThreads, 4) void score_kernel(ScoreArgs a, int n_row_tiles, int run_len, int n_runs, int blocks_per_xcd)
+__global__ __launch_bounds__(kScoreThreads, 4) void score_kernel(ScoreArgs a, int n_row_tiles, int run_len, int n_runs, int blocks_per_xcd,
+                                                                   int by_row)
 {
     // two bf16 K buffers (hi rows, then lo rows); the fp32 q staging shares the second
     __shared__ __align__(16) uint8_t lds[kLdsBytes];
     float (*sq)[kQPitch] = (float (*)[kQPitch])(lds + kKBytes);
 
-    const int lb = (blockIdx.x & 7) * blocks_per_xcd + (blockIdx.x >> 3);
-    if (lb >= n_row_tiles * n_runs)
-        return;                              // uniform over the workgroup
-    const int run = lb / n_row_tiles;
-    const int rt = lb - run * n_row_tiles;
+    int run, rt;
+    if (by_row) {
+        // XCD x (workgroup id mod 8) takes row tiles x, x + 8, ..., each with all its runs
+        const int i = blockIdx.x >> 3;
+        const int m = i / n_runs;
+        run = i - m * n_runs;
+        rt = (blockIdx.x & 7) + 8 * m;
+        if (rt >= n_row_tiles)
+            return;                          // uniform over the workgroup
+    } else {
+        // XCD x takes a contiguous range of runs, each with all its row tiles
+        const int lb = (blockIdx.x & 7) * blocks_per_xcd + (blockIdx.x >> 3);
+        if (lb >= n_row_tiles * n_runs)
+            return;
+        run = lb / n_row_tiles;
+        rt = lb - run * n_row_tiles;
+    }
     const int r0 = rt * kTile;
     const int last_row = min(a.T, r0 + kTile) - 1;
     const int64_t last_causal = (int64_t)a.pos0 + last_row;
@@ -302,8 +315,30 @@ hipError_t launch_score(const ScoreArgs &a, hipStream_t stream)
     const int run_len = std::max(min_run, (n_col_tiles + want_runs - 1) / want_runs);
     const int n_runs = (n_col_tiles + run_len - 1) / run_len;
     const int64_t blocks = (int64_t)n_runs * n_row_tiles;
-    const int per_xcd = (int)((blocks + 7) / 8);
-    hipLaunchKernelGGL(score_kernel, dim3(8 * per_xcd), dim3(kScoreThreads), 0, stream, a, n_row_tiles, run_len, n_runs, per_xcd);
+    const int run_major_per_xcd = (int)((blocks + 7) / 8);
+
+    // Column tiles per XCD under both workgroup orders. Runs on one XCD keep
+    // the K rows it reads within its own L2, which long contexts need (each
+    // XCD reads an eighth of K); but where row lengths differ (a causal
+    // triangle near the start of a sequence) whole runs hold little or no
+    // work, and XCDs that each take every eighth row tile balance it.
+    int64_t by_runs[8] = {}, by_rows[8] = {};
+    for (int rt = 0; rt < n_row_tiles; ++rt) {
+        const int64_t last_tile = ((int64_t)a.pos0 + std::min(a.T, (rt + 1) * kTile) - 1) / kTile;
+        for (int run = 0; run < n_runs; ++run) {
+            const int64_t lo = (int64_t)run * run_len;
+            const int64_t hi = std::min<int64_t>(lo + run_len, n_col_tiles) - 1;
+            const int64_t w = std::max<int64_t>(0, std::min(hi, last_tile) - lo + 1);
+            by_runs[((int64_t)run * n_row_tiles + rt) / run_major_per_xcd] += w;
+            by_rows[rt & 7] += w;
+        }
+    }
+    const int64_t max_runs = *std::max_element(by_runs, by_runs + 8);
+    const int64_t max_rows = *std::max_element(by_rows, by_rows + 8);
+    const int by_row = n_row_tiles >= 8 && 8 * max_rows < 7 * max_runs;
+    const int per_xcd = by_row ? ((n_row_tiles + 7) / 8) * n_runs : run_major_per_xcd;
+    hipLaunchKernelGGL(score_kernel, dim3(8 * per_xcd), dim3(kScoreThreads), 0, stream, a, n_row_tiles, run_len, n_runs,
+                       run_major_per_xcd, by_row);
     return hipGetLastError();
 }
 
