@@ -33,6 +33,17 @@ def test_edge_shapes_and_tails(T, pos0, Hs, extra, dead):
     check_score_case(sc, n_sample=64)
 
 
+
+@pytest.mark.parametrize("T,pos0,Hs,extra", [(1000, 0, 3, 7), (777, 13, 12, 0), (1999, 77, 5, 65), (900, 4000, 2, 1)])
+def test_ragged_row_tiles_in_both_workgroup_orders(T, pos0, Hs, extra):
+    """Row counts off the 64-row grid with eight or more row tiles. The first
+    three take the order in which XCDs own every eighth row tile (their causal
+    rows differ a lot in length), the last the run-major order; every row's
+    extents are checked, and the values of 24 rows against the oracle."""
+    sc = synth.score_case(T=T, pos0=pos0, Hs=Hs, row_stride=pos0 + T + extra, seed=T + 7 * pos0, scale=0.6)
+    print("score ragged T=%d pos0=%d worst err/A %g" % (T, pos0, check_score_case(sc, n_sample=24, seed=T)),
+          flush=True)
+
 def test_integer_scores_are_exact():
     T, pos0, Hs = 100, 30, 4
     rng = np.random.default_rng(1)
