@@ -481,16 +481,26 @@ def main():
         sc = synth.score_case(T=T, pos0=case.pos0, Hs=12)
         sq, sk = up(sc.q), up(sc.k)
         scores = torch.empty(T, sc.row_stride, dtype=torch.float32, device=dev)
+        # qsa_score, alternating launch by launch with qsa_score_ws (the same
+        # scores, q's heads summed once into a workspace by a first pass; both
+        # of its kernels inside its timed region)
+        ws = torch.empty(qsa.qsa_score_ws_bytes(T), dtype=torch.uint8, device=dev)
         for _ in range(2):
             qsa.qsa_score(sq, sk, sc.pos0, 1.0, float("-inf"), scores, stream=stream)
+            qsa.qsa_score_ws(sq, sk, sc.pos0, 1.0, float("-inf"), scores, ws, stream=stream)
         reps = 10
         sev = [[ev(), ev()] for _ in range(reps)]
-        for e in sev:
+        wev = [[ev(), ev()] for _ in range(reps)]
+        for e, f in zip(sev, wev):
             e[0].record(stream)
             qsa.qsa_score(sq, sk, sc.pos0, 1.0, float("-inf"), scores, stream=stream)
             e[1].record(stream)
+            f[0].record(stream)
+            qsa.qsa_score_ws(sq, sk, sc.pos0, 1.0, float("-inf"), scores, ws, stream=stream)
+            f[1].record(stream)
         torch.cuda.synchronize()
         s_us = [1e3 * e[0].elapsed_time(e[1]) for e in sev]
+        w_us = [1e3 * e[0].elapsed_time(e[1]) for e in wev]
         us = float(np.mean(s_us))
         e0, e1 = ev(), ev()
         flops = 2.0 * 128 * sum(case.pos0 + t + 1 for t in range(T))   # heads summed before the contraction
@@ -518,6 +528,21 @@ def main():
             "other_roofline": mfma_roof if t_hbm >= t_mfma else hbm_roof,
             "lower_bound_us": {"hbm": t_hbm * 1e6, "bf16_mfma": t_mfma * 1e6},
         }
+        wavg = float(np.mean(w_us))
+        ref = torch.full_like(scores, float("nan"))
+        alt = torch.full_like(scores, float("nan"))
+        qsa.qsa_score(sq, sk, sc.pos0, 1.0, float("-inf"), ref, stream=stream)
+        qsa.qsa_score_ws(sq, sk, sc.pos0, 1.0, float("-inf"), alt, ws, stream=stream)
+        torch.cuda.synchronize()
+        result["companion_score"]["with_workspace"] = {
+            "entry": "qsa_score_ws", "workspace_bytes": int(ws.numel()), "avg_us": wavg, "us": stats(w_us),
+            "roofline": {"bound": "hbm", "achieved": score_bytes / (wavg * 1e-6) / 1e9, "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": score_bytes / (wavg * 1e-6) / 1e9 / HBM_PEAK_GBS},
+            "bitwise_equal_to_qsa_score": bool(torch.equal(ref.view(torch.int32), alt.view(torch.int32))),
+            "over_qsa_score_median": float(np.median(w_us) / np.median(s_us)),
+            "note": "timed alternating launch by launch with qsa_score",
+        }
+        del ref, alt, ws
         if not args.no_cpu:
             print("bench: score errors against the oracle", file=sys.stderr, flush=True)
             result["companion_score"]["errors"] = score_errors(sc, scores.cpu().numpy(), 24, host_cpu()[0])

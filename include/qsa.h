@@ -202,6 +202,38 @@ QSA_API qsa_status qsa_score(const float *q, const float *k, int32_t n_cells, in
                      float *scores, int64_t row_stride, void *stream);
 
 /*
+ * qsa_score_ws_bytes -- bytes of the workspace qsa_score_ws takes for T rows:
+ * 512 per row, for T rounded up to a multiple of 64 (0 when T <= 0).
+ */
+QSA_API int64_t qsa_score_ws_bytes(int32_t T);
+
+/*
+ * qsa_score_ws -- qsa_score with the head sum of q taken once per row.
+ *
+ * Computes what qsa_score computes (same definition, pages and sections as
+ * above), to the same bits. qsa_score sums the heads of a 64-row block of q in
+ * every workgroup that walks one of the block's column runs (16 such runs at
+ * 1984 rows, pos0 = 30000). Here a first pass writes each row's head sum,
+ * times scale and split into bf16 parts, to `workspace`, and the walk reads
+ * it from there. The library takes that pass only where it pays: where q
+ * (T * Hs * D * 4 bytes) is 4 MB or more and the workgroup order it picks has
+ * every XCD read all of q. Otherwise the call runs as qsa_score does and
+ * leaves the workspace untouched.
+ *
+ * workspace  device memory of ws_bytes >= qsa_score_ws_bytes(T) bytes,
+ *            16-byte aligned, owned by the caller; its contents are
+ *            overwritten and mean nothing to the caller afterwards. Calls that
+ *            share a workspace must be ordered (one stream, or synchronised).
+ * The other arguments, their layouts and the errors are those of qsa_score;
+ * a NULL, short or misaligned workspace returns QSA_ERR_ARG before anything
+ * is enqueued.
+ */
+QSA_API qsa_status qsa_score_ws(const float *q, const float *k, int32_t n_cells, int32_t pos0,
+                        int32_t T, int32_t Hs, int32_t D, float scale, float dead,
+                        float *scores, int64_t row_stride, void *workspace, int64_t ws_bytes,
+                        void *stream);
+
+/*
  * qsa_quant_append -- write fp32 K and V rows into the int8 cache with one
  * fp16 scale per 32-element group.
  *

@@ -16,7 +16,7 @@ import torch
 
 __all__ = [
     "QsaError", "CHUNK", "GROUP", "HEAD_DIM",
-    "qsa_attn", "qsa_attn_merge", "qsa_attn_merge_gated", "qsa_merge", "qsa_merge_gated", "qsa_split_merge_static", "qsa_score", "qsa_quant_append", "qsa_select", "qsa_part_bytes",
+    "qsa_attn", "qsa_attn_merge", "qsa_attn_merge_gated", "qsa_merge", "qsa_merge_gated", "qsa_split_merge_static", "qsa_score", "qsa_score_ws", "qsa_score_ws_bytes", "qsa_quant_append", "qsa_select", "qsa_part_bytes",
     "qsa_part_offsets",
     "qsa_last_error",
     "alloc_part", "part_views", "chunk_count", "lib", "LIB_PATH",
@@ -62,6 +62,10 @@ def lib() -> ctypes.CDLL:
         L.qsa_split_merge_static.restype = ctypes.c_int
         L.qsa_score.argtypes = [P, P, i32, i32, i32, i32, i32, f32, f32, P, i64, P]
         L.qsa_score.restype = ctypes.c_int
+        L.qsa_score_ws.argtypes = [P, P, i32, i32, i32, i32, i32, f32, f32, P, i64, P, i64, P]
+        L.qsa_score_ws.restype = ctypes.c_int
+        L.qsa_score_ws_bytes.argtypes = [i32]
+        L.qsa_score_ws_bytes.restype = i64
         L.qsa_quant_append.argtypes = [P, P, i32, i32, P, P, P, P, i32, i32, P]
         L.qsa_quant_append.restype = ctypes.c_int
         L.qsa_select.argtypes = [P, i64, i32, i32, i32, P, i32, P]
@@ -273,6 +277,28 @@ def qsa_score(q: torch.Tensor, k: torch.Tensor, pos0: int, scale: float, dead: f
         raise ValueError("scores must have T rows")
     _raise_on(lib().qsa_score(_ptr(q), _ptr(k), k.shape[0], pos0, T, Hs, D, float(scale), float(dead),
                               _ptr(scores), scores.shape[1], _stream(stream)))
+
+
+def qsa_score_ws_bytes(T: int) -> int:
+    return int(lib().qsa_score_ws_bytes(T))
+
+
+def qsa_score_ws(q: torch.Tensor, k: torch.Tensor, pos0: int, scale: float, dead: float,
+                 scores: torch.Tensor, workspace: torch.Tensor, stream=None) -> None:
+    """qsa_score with the head sum of q taken once, through workspace (a contiguous
+    byte tensor on the same device, at least qsa_score_ws_bytes(T) bytes)."""
+    _need(q, "q", torch.float32, 3)
+    _need(k, "k", torch.float32, 2)
+    _need(scores, "scores", torch.float32, 2)
+    _need(workspace, "workspace", torch.uint8, 1)
+    T, Hs, D = q.shape
+    if k.shape[1] != D:
+        raise ValueError("k must be [n_cells][%d]" % D)
+    if scores.shape[0] != T:
+        raise ValueError("scores must have T rows")
+    _raise_on(lib().qsa_score_ws(_ptr(q), _ptr(k), k.shape[0], pos0, T, Hs, D, float(scale), float(dead),
+                                 _ptr(scores), scores.shape[1], _ptr(workspace), workspace.numel(),
+                                 _stream(stream)))
 
 
 def qsa_quant_append(k: torch.Tensor, v: torch.Tensor, kq: torch.Tensor, vq: torch.Tensor, ksc: torch.Tensor,

@@ -315,33 +315,44 @@ qsa_status qsa_merge_gated(const void *part, int32_t n_chunks, int32_t T, int32_
     return merge_impl("qsa_merge_gated", part, n_chunks, T, H, D, gate, out, sums16, true, stream);
 }
 
-qsa_status qsa_score(const float *q, const float *k, int32_t n_cells, int32_t pos0,
-                     int32_t T, int32_t Hs, int32_t D, float scale, float dead,
-                     float *scores, int64_t row_stride, void *stream)
+namespace {
+
+qsa_status score_impl(const char *fn, const float *q, const float *k, int32_t n_cells, int32_t pos0, int32_t T,
+                      int32_t Hs, int32_t D, float scale, float dead, float *scores, int64_t row_stride,
+                      bool with_ws, void *ws, int64_t ws_bytes, void *stream)
 {
     if (T < 0 || pos0 < 0 || n_cells < 0)
-        return fail(QSA_ERR_ARG, "qsa_score: negative T (%d), pos0 (%d) or n_cells (%d)", T, pos0, n_cells);
+        return fail(QSA_ERR_ARG, "%s: negative T (%d), pos0 (%d) or n_cells (%d)", fn, T, pos0, n_cells);
     if (Hs < 1)
-        return fail(QSA_ERR_ARG, "qsa_score: Hs must be >= 1 (got %d)", Hs);
+        return fail(QSA_ERR_ARG, "%s: Hs must be >= 1 (got %d)", fn, Hs);
     if (Hs > qsa::kMaxHeads)
-        return fail(QSA_ERR_UNSUPPORTED, "qsa_score: at most %d heads (got %d)", qsa::kMaxHeads, Hs);
+        return fail(QSA_ERR_UNSUPPORTED, "%s: at most %d heads (got %d)", fn, qsa::kMaxHeads, Hs);
     if (D != qsa::kD)
-        return fail(QSA_ERR_UNSUPPORTED, "qsa_score: head dim %d not implemented (only %d)", D, qsa::kD);
+        return fail(QSA_ERR_UNSUPPORTED, "%s: head dim %d not implemented (only %d)", fn, D, qsa::kD);
     if ((int64_t)pos0 + T > INT32_MAX)
-        return fail(QSA_ERR_ARG, "qsa_score: pos0 + T overflows int32");
+        return fail(QSA_ERR_ARG, "%s: pos0 + T overflows int32", fn);
     if ((int64_t)n_cells < (int64_t)pos0 + T)
-        return fail(QSA_ERR_ARG, "qsa_score: n_cells (%d) < pos0 + T (%lld)", n_cells, (long long)pos0 + T);
+        return fail(QSA_ERR_ARG, "%s: n_cells (%d) < pos0 + T (%lld)", fn, n_cells, (long long)pos0 + T);
     if (row_stride < (int64_t)pos0 + T)
-        return fail(QSA_ERR_ARG, "qsa_score: row_stride (%lld) < pos0 + T (%lld)", (long long)row_stride,
+        return fail(QSA_ERR_ARG, "%s: row_stride (%lld) < pos0 + T (%lld)", fn, (long long)row_stride,
                     (long long)pos0 + T);
     if (((int64_t)T + 63) / 64 > 65535)
-        return fail(QSA_ERR_ARG, "qsa_score: T too large for one launch");
+        return fail(QSA_ERR_ARG, "%s: T too large for one launch", fn);
     if (T == 0)
         return ok();
     if (!q || !k || !scores)
-        return fail(QSA_ERR_ARG, "qsa_score: NULL q, k or scores");
+        return fail(QSA_ERR_ARG, "%s: NULL q, k or scores", fn);
     if (!aligned(q, 16) || !aligned(k, 16) || !aligned(scores, 4))
-        return fail(QSA_ERR_ARG, "qsa_score: misaligned pointer (q, k: 16 B; scores: 4 B)");
+        return fail(QSA_ERR_ARG, "%s: misaligned pointer (q, k: 16 B; scores: 4 B)", fn);
+    if (with_ws) {
+        if (ws_bytes < qsa::score_ws_bytes(T))
+            return fail(QSA_ERR_ARG, "%s: workspace of %lld bytes, %lld needed for %d rows", fn, (long long)ws_bytes,
+                        (long long)qsa::score_ws_bytes(T), T);
+        if (!ws)
+            return fail(QSA_ERR_ARG, "%s: NULL workspace", fn);
+        if (!aligned(ws, 16))
+            return fail(QSA_ERR_ARG, "%s: misaligned workspace (16 B)", fn);
+    }
     qsa_status st = check_device();
     if (st != QSA_OK)
         return st;
@@ -356,7 +367,30 @@ qsa_status qsa_score(const float *q, const float *k, int32_t n_cells, int32_t po
     a.dead = dead;
     a.scores = scores;
     a.row_stride = row_stride;
-    return launched(qsa::launch_score(a, static_cast<hipStream_t>(stream)), "qsa_score");
+    return launched(qsa::launch_score(a, with_ws ? ws : nullptr, static_cast<hipStream_t>(stream)), fn);
+}
+
+} // namespace
+
+qsa_status qsa_score(const float *q, const float *k, int32_t n_cells, int32_t pos0,
+                     int32_t T, int32_t Hs, int32_t D, float scale, float dead,
+                     float *scores, int64_t row_stride, void *stream)
+{
+    return score_impl("qsa_score", q, k, n_cells, pos0, T, Hs, D, scale, dead, scores, row_stride, false, nullptr, 0,
+                      stream);
+}
+
+int64_t qsa_score_ws_bytes(int32_t T)
+{
+    return qsa::score_ws_bytes(T);
+}
+
+qsa_status qsa_score_ws(const float *q, const float *k, int32_t n_cells, int32_t pos0,
+                        int32_t T, int32_t Hs, int32_t D, float scale, float dead,
+                        float *scores, int64_t row_stride, void *workspace, int64_t ws_bytes, void *stream)
+{
+    return score_impl("qsa_score_ws", q, k, n_cells, pos0, T, Hs, D, scale, dead, scores, row_stride, true, workspace,
+                      ws_bytes, stream);
 }
 
 qsa_status qsa_quant_append(const float *k, const float *v, int32_t n_rows, int32_t D,

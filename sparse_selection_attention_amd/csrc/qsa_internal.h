@@ -96,7 +96,9 @@ hipError_t launch_attn_merge(const AttnArgs &a, hipStream_t stream);
 hipError_t launch_attn_tile(const AttnArgs &a, hipStream_t stream);
 hipError_t launch_attn_merge_tile(const AttnArgs &a, hipStream_t stream);
 hipError_t launch_merge(const MergeArgs &a, hipStream_t stream);
-hipError_t launch_score(const ScoreArgs &a, hipStream_t stream);
+// ws: nullptr, or score_ws_bytes(a.T) bytes of device memory for the prepared q operands
+hipError_t launch_score(const ScoreArgs &a, void *ws, hipStream_t stream);
+inline int64_t score_ws_bytes(int32_t T) { return T <= 0 ? 0 : (((int64_t)T + 63) / 64) * 64 * 512; }
 hipError_t launch_quant(const QuantArgs &a, hipStream_t stream);
 hipError_t launch_select(const SelectArgs &a, hipStream_t stream);
 

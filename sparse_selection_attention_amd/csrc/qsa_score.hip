@@ -46,8 +46,18 @@
 // read by a later kernel, so it streams past the caches instead of evicting
 // the K rows that the other workgroups are still reading.
 // Workgroups are ordered so that each XCD (workgroup id mod 8) walks a
-// contiguous range of column runs: the K rows one XCD reads stay within its
-// own L2.
+// contiguous range of column runs, and the K rows one XCD reads stay within
+// its own L2; where that leaves the XCDs unbalanced (rows of very different
+// lengths near the start of a sequence), each XCD takes every eighth row tile
+// instead.
+//
+// Every workgroup that walks a run of a row tile sums that tile's heads, so q
+// is read once per run (16 times at 1984 rows), in a burst when the launch
+// starts, before any walk. With a workspace (qsa_score_ws) a first pass sums
+// each 16-row strip's heads once, scales and splits them, and writes the
+// operands in the order the walk's waves hold them; the walk then loads its
+// operands with eight 16-byte reads per lane. Both paths add the heads in the
+// same order and split the same values, so their scores are the same bits.
 #include "qsa_internal.h"
 
 #include <algorithm>
@@ -70,13 +80,17 @@ constexpr int kKBytes = 2 * kTile * kKPitch * 2;          // one K tile: hi rows
 static_assert(kQBytes <= kKBytes, "the q staging fits in one K buffer");
 constexpr int kLdsBytes = 2 * kKBytes;                     // two K buffers
 constexpr float kBf16Max = 3.38953139e38f;   // largest finite bf16, 0x7f7f
+constexpr int64_t kPrepareBytes = int64_t(4) << 20;   // q size from which qsa_score_ws sums heads first
 
 typedef float float2v __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
-// x = hi + lo as above, for two values (one packed conversion for each part)
+// x = hi + lo as above, for two values (one packed conversion for each part).
+// No contraction: x - hi is a subtraction of the rounded x, whatever product x
+// came from, so every caller splits the same value the same way.
 __device__ inline void split2(float x0, float x1, bf16x2 &hi, bf16x2 &lo)
 {
+#pragma clang fp contract(off)
     const float2v c = {__builtin_amdgcn_fmed3f(x0, -kBf16Max, kBf16Max),
                        __builtin_amdgcn_fmed3f(x1, -kBf16Max, kBf16Max)};
     hi = __builtin_convertvector(c, bf16x2);
@@ -104,6 +118,75 @@ __device__ inline void split4(const floatx4 &a, bf16x4 &hi, bf16x4 &lo)
     lo = (bf16x4){l[0][0], l[0][1], l[1][0], l[1][1]};
 }
 
+// q rows r0 .. r0 + R - 1 summed over heads into rows[0 .. R - 1] (zero for
+// rows at or past T), by the NT threads of a workgroup, a float4 per
+// thread-step
+template <int R, int NT>
+__device__ inline void sum_heads(const ScoreArgs &a, int r0, float (*rows)[kQPitch], int tid)
+{
+    for (int idx = tid; idx < R * (kD / 4); idx += NT) {
+        const int row = idx >> 5, c4 = idx & 31;
+        float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+        const int t = r0 + row;
+        if (t < a.T) {
+            // every head's read is issued before the first add (one round trip
+            // per row, not one per few heads); the adds keep head order
+            const float *qr = a.q + (int64_t)t * a.Hs * kD + 4 * c4;
+            // (heads go in groups of four, each group behind one uniform branch;
+            // inside a group, indexes past Hs re-read the last head, with no
+            // branch per load; those values are not added)
+            float4 v[kMaxHeads];
+#pragma unroll
+            for (int h4 = 0; h4 < kMaxHeads; h4 += 4)
+                if (h4 < a.Hs) {                     // uniform: groups of four heads that hold a head
+#pragma unroll
+                    for (int h = h4; h < h4 + 4; ++h)
+                        v[h] = *(const float4 *)(qr + (int64_t)min(h, a.Hs - 1) * kD);
+                }
+#pragma unroll
+            for (int h = 0; h < kMaxHeads; ++h)
+                if (h < a.Hs) {
+                    acc.x += v[h].x; acc.y += v[h].y; acc.z += v[h].z; acc.w += v[h].w;
+                }
+        }
+        *(float4 *)&rows[row][4 * c4] = acc;
+    }
+}
+
+// the A operand of lane (j, c16) for k-step ks: the staged head sum of row
+// c16 of `rows`, dims 32 ks + 8j .. +7, times the score scale (scale * (q . k)
+// = (scale * q) . k), split into bf16 parts
+__device__ inline void a_operand(const ScoreArgs &a, const float (*rows)[kQPitch], int ks, int j, int c16,
+                                 bf16x8 &hi, bf16x8 &lo)
+{
+    const float *src = &rows[c16][32 * ks + 8 * j];
+    float4 u = *(const float4 *)src, v = *(const float4 *)(src + 4);
+    u.x *= a.scale; u.y *= a.scale; u.z *= a.scale; u.w *= a.scale;
+    v.x *= a.scale; v.y *= a.scale; v.z *= a.scale; v.w *= a.scale;
+    split8(u, v, hi, lo);
+}
+
+// Workspace of the prepared path: per 16-row strip, k-step and part (hi, lo),
+// the 64 lanes' 16-byte operands: entry ((strip * 4 + ks) * 2 + part) * 64 + lane.
+constexpr int kStripOperands = 4 * 2 * 64;       // uint4 entries per strip (8 KB)
+
+// One 16-row strip: its heads summed into LDS, then wave ks writes the
+// operands of k-step ks. Rows past T get zero operands (never multiplied
+// into a written score).
+__global__ __launch_bounds__(256) void prep_kernel(ScoreArgs a, uint4 *ws)
+{
+    __shared__ __align__(16) float sq[16][kQPitch];
+    const int strip = blockIdx.x, tid = threadIdx.x;
+    sum_heads<16, 256>(a, 16 * strip, sq, tid);
+    __syncthreads();
+    const int lane = tid & 63, ks = tid >> 6;
+    bf16x8 hi, lo;
+    a_operand(a, sq, ks, lane >> 4, lane & 15, hi, lo);
+    uint4 *dst = ws + (int64_t)strip * kStripOperands + ks * 128 + lane;
+    dst[0] = __builtin_bit_cast(uint4, hi);
+    dst[64] = __builtin_bit_cast(uint4, lo);
+}
+
 // the thread's staged K values (rows (tid >> 5) + 16i, column 4 * (tid & 31))
 // split into bf16 high and low parts, into the K buffer at `buf`
 __device__ inline void stage_k(uint8_t *buf, const floatx4 (&kreg)[4], int tid)
@@ -119,8 +202,9 @@ __device__ inline void stage_k(uint8_t *buf, const floatx4 (&kreg)[4], int tid)
     }
 }
 
+template <bool kPrepared>
 __global__ __launch_bounds__(kScoreThreads, 4) void score_kernel(ScoreArgs a, int n_row_tiles, int run_len, int n_runs, int blocks_per_xcd,
-                                                                   int by_row)
+                                                                   int by_row, const uint4 *ws)
 {
     // two bf16 K buffers (hi rows, then lo rows); the fp32 q staging shares the second
     __shared__ __align__(16) uint8_t lds[kLdsBytes];
@@ -153,34 +237,8 @@ __global__ __launch_bounds__(kScoreThreads, 4) void score_kernel(ScoreArgs a, in
         return;
 
     const int tid = threadIdx.x;
-    // q rows of this tile, summed over heads, float4 per thread-step
-    for (int idx = tid; idx < kTile * (kD / 4); idx += kScoreThreads) {
-        const int row = idx >> 5, c4 = idx & 31;
-        float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-        const int t = r0 + row;
-        if (t < a.T) {
-            // every head's read is issued before the first add (one round trip
-            // per row, not one per few heads); the adds keep head order
-            const float *qr = a.q + (int64_t)t * a.Hs * kD + 4 * c4;
-            // (heads go in groups of four, each group behind one uniform branch;
-            // inside a group, indexes past Hs re-read the last head, with no
-            // branch per load; those values are not added)
-            float4 v[kMaxHeads];
-#pragma unroll
-            for (int h4 = 0; h4 < kMaxHeads; h4 += 4)
-                if (h4 < a.Hs) {                     // uniform: groups of four heads that hold a head
-#pragma unroll
-                    for (int h = h4; h < h4 + 4; ++h)
-                        v[h] = *(const float4 *)(qr + (int64_t)min(h, a.Hs - 1) * kD);
-                }
-#pragma unroll
-            for (int h = 0; h < kMaxHeads; ++h)
-                if (h < a.Hs) {
-                    acc.x += v[h].x; acc.y += v[h].y; acc.z += v[h].z; acc.w += v[h].w;
-                }
-        }
-        *(float4 *)&sq[row][4 * c4] = acc;
-    }
+    if constexpr (!kPrepared)
+        sum_heads<kTile, kScoreThreads>(a, r0, sq, tid);   // q rows of this tile, summed over heads
 
     // K tile staging: thread tid moves 4 float4s, rows (tid >> 5) + 16i, column 4 * (tid & 31)
     floatx4 kreg[4];
@@ -203,16 +261,19 @@ __global__ __launch_bounds__(kScoreThreads, 4) void score_kernel(ScoreArgs a, in
     const bool live = r0 + rq < a.T;                     // uniform: a strip past the last row only stages
 
     // A operands, held for the whole walk: row rq + c16, dims 32 ks + 8j .. +7
-    __syncthreads();
     bf16x8 ah[4], al[4];
+    if constexpr (kPrepared) {
+        const uint4 *src = ws + (int64_t)(4 * rt + (w >> 1)) * kStripOperands + lane;
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-        // the score scale goes on q here, once: scale * (q . k) = (scale * q) . k
-        const float *src = &sq[rq + c16][32 * ks + 8 * j];
-        float4 u = *(const float4 *)src, v = *(const float4 *)(src + 4);
-        u.x *= a.scale; u.y *= a.scale; u.z *= a.scale; u.w *= a.scale;
-        v.x *= a.scale; v.y *= a.scale; v.z *= a.scale; v.w *= a.scale;
-        split8(u, v, ah[ks], al[ks]);
+        for (int ks = 0; ks < 4; ++ks) {
+            ah[ks] = __builtin_bit_cast(bf16x8, src[ks * 128]);
+            al[ks] = __builtin_bit_cast(bf16x8, src[ks * 128 + 64]);
+        }
+    } else {
+        __syncthreads();
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+            a_operand(a, sq + rq, ks, j, c16, ah[ks], al[ks]);
     }
     stage_k(lds, kreg, tid);                 // the first tile into buffer 0
     __syncthreads();                         // buffer 0 complete; the q staging is free
@@ -299,7 +360,7 @@ __global__ __launch_bounds__(kScoreThreads, 4) void score_kernel(ScoreArgs a, in
 
 } // namespace
 
-hipError_t launch_score(const ScoreArgs &a, hipStream_t stream)
+hipError_t launch_score(const ScoreArgs &a, void *ws, hipStream_t stream)
 {
     const int64_t cells = (int64_t)a.pos0 + a.T;
     const int n_col_tiles = (int)((cells + kTile - 1) / kTile);
@@ -337,8 +398,22 @@ hipError_t launch_score(const ScoreArgs &a, hipStream_t stream)
     const int64_t max_rows = *std::max_element(by_rows, by_rows + 8);
     const int by_row = n_row_tiles >= 8 && 8 * max_rows < 7 * max_runs;
     const int per_xcd = by_row ? ((n_row_tiles + 7) / 8) * n_runs : run_major_per_xcd;
-    hipLaunchKernelGGL(score_kernel, dim3(8 * per_xcd), dim3(kScoreThreads), 0, stream, a, n_row_tiles, run_len, n_runs,
-                       run_major_per_xcd, by_row);
+    // The first pass pays where the walk's workgroups would read q from beyond
+    // L2 many times over: in the run-major order every XCD reads all of q
+    // (eight times q's size in L2 misses, 96 MB at 1984 rows of 12 heads);
+    // with a small q (decode steps, one head) or in the row-major order (each
+    // XCD reads an eighth of q) the extra launch costs more than it saves.
+    const bool prepare = ws && !by_row && (int64_t)a.T * a.Hs * kD * 4 >= kPrepareBytes;
+    if (prepare) {
+        // one strip of operands per 16 rows of every row tile (the last tile's
+        // rows past T included), so the walk's reads stay inside the workspace
+        hipLaunchKernelGGL(prep_kernel, dim3(4 * n_row_tiles), dim3(256), 0, stream, a, (uint4 *)ws);
+        hipLaunchKernelGGL(score_kernel<true>, dim3(8 * per_xcd), dim3(kScoreThreads), 0, stream, a, n_row_tiles,
+                           run_len, n_runs, run_major_per_xcd, by_row, (const uint4 *)ws);
+    } else {
+        hipLaunchKernelGGL(score_kernel<false>, dim3(8 * per_xcd), dim3(kScoreThreads), 0, stream, a, n_row_tiles,
+                           run_len, n_runs, run_major_per_xcd, by_row, (const uint4 *)nullptr);
+    }
     return hipGetLastError();
 }
 

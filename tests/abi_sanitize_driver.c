@@ -87,6 +87,15 @@ int main(void)
            "score Hs = 17");
     expect(qsa_score(AT(4), FAKE, 100, 10, 4, 12, 128, 1.0f, -1.0f, FAKE, 100, NULL), QSA_ERR_ARG,
            "score misaligned q");
+    expect(qsa_score_ws_bytes(65) == 65536 ? QSA_OK : QSA_ERR_ARG, QSA_OK, "score workspace bytes");
+    expect(qsa_score_ws(FAKE, FAKE, 100, 10, 0, 12, 128, 1.0f, -1.0f, FAKE, 100, NULL, 0, NULL), QSA_OK,
+           "score_ws T = 0");
+    expect(qsa_score_ws(FAKE, FAKE, 100, 10, 4, 12, 128, 1.0f, -1.0f, FAKE, 100, FAKE, 32767, NULL), QSA_ERR_ARG,
+           "score_ws short workspace");
+    expect(qsa_score_ws(FAKE, FAKE, 100, 10, 4, 12, 128, 1.0f, -1.0f, FAKE, 100, NULL, 32768, NULL), QSA_ERR_ARG,
+           "score_ws NULL workspace");
+    expect(qsa_score_ws(FAKE, FAKE, 100, 10, 4, 12, 128, 1.0f, -1.0f, FAKE, 100, AT(8), 32768, NULL), QSA_ERR_ARG,
+           "score_ws misaligned workspace");
 
     /* cache writer */
     expect(qsa_quant_append(FAKE, FAKE, 0, 128, FAKE, FAKE, FAKE, FAKE, 0, 10, NULL), QSA_OK, "quant n_rows = 0");

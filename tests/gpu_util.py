@@ -156,16 +156,23 @@ def check_attn_case(case: synth.AttnCase, n_sample=20, records=True, implicit=Fa
     return worst
 
 
-def run_score(sc: synth.ScoreCase, fill=np.nan):
+def run_score(sc: synth.ScoreCase, fill=np.nan, workspace=None):
+    """qsa_score, or qsa_score_ws through `workspace` (a device byte tensor, or
+    True for a fresh one filled with a byte pattern rather than zeros)."""
     q, k = to_dev(sc.q), to_dev(sc.k)
     scores = torch.full((sc.T, sc.row_stride), float(fill), dtype=torch.float32, device=dev())
-    qsa.qsa_score(q, k, sc.pos0, float(sc.scale), float(sc.dead), scores)
+    if workspace is None:
+        qsa.qsa_score(q, k, sc.pos0, float(sc.scale), float(sc.dead), scores)
+    else:
+        if workspace is True:
+            workspace = torch.full((max(qsa.qsa_score_ws_bytes(sc.T), 1),), 0xA5, dtype=torch.uint8, device=dev())
+        qsa.qsa_score_ws(q, k, sc.pos0, float(sc.scale), float(sc.dead), scores, workspace)
     torch.cuda.synchronize()
     return scores.cpu().numpy()
 
 
-def check_score_case(sc: synth.ScoreCase, n_sample=16, seed=0):
-    g = run_score(sc)
+def check_score_case(sc: synth.ScoreCase, n_sample=16, seed=0, workspace=None):
+    g = run_score(sc, workspace=workspace)
     T = sc.T
     # extents for every row: causal cells finite, the tail holds `dead`, the rest untouched
     for t in range(T):

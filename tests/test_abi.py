@@ -24,7 +24,8 @@ def declared_symbols():
 def test_library_loads_and_exports_every_declared_symbol():
     L = qsa.lib()
     names = declared_symbols()
-    assert {"qsa_attn", "qsa_attn_merge", "qsa_merge", "qsa_score", "qsa_quant_append", "qsa_select",
+    assert {"qsa_attn", "qsa_attn_merge", "qsa_merge", "qsa_score", "qsa_score_ws", "qsa_score_ws_bytes",
+            "qsa_quant_append", "qsa_select",
             "qsa_merge_gated", "qsa_attn_merge_gated",
             "qsa_part_bytes", "qsa_part_offsets", "qsa_last_error"} <= names
     for n in names:
@@ -104,6 +105,8 @@ def test_zero_tokens_is_a_no_op():
     P = ctypes.c_void_p
     assert qsa.lib().qsa_merge(P(None), 5, 0, 12, 128, P(None), P(None)) == qsa.QSA_OK
     assert qsa.lib().qsa_score(P(None), P(None), 10, 10, 0, 1, 128, 1.0, 0.0, P(None), 10, P(None)) == qsa.QSA_OK
+    assert qsa.lib().qsa_score_ws(P(None), P(None), 10, 10, 0, 1, 128, 1.0, 0.0, P(None), 10, P(None), 0,
+                                  P(None)) == qsa.QSA_OK
 
 
 @pytest.mark.parametrize("args,status", [
@@ -152,6 +155,31 @@ def score(**kw):
 def test_score_rejects_bad_arguments_on_host(kw, status):
     assert score(**kw) == status
     assert qsa.qsa_last_error().startswith("qsa_score")
+    assert score_ws(**kw) == status
+    assert qsa.qsa_last_error().startswith("qsa_score_ws")
+
+
+def score_ws(**kw):
+    a = dict(q=FAKE, k=FAKE, n_cells=100, pos0=10, T=4, Hs=1, D=128, scale=1.0, dead=-1.0, scores=FAKE,
+             row_stride=14, ws=FAKE, ws_bytes=64 * 512)
+    a.update(kw)
+    P = ctypes.c_void_p
+    return qsa.lib().qsa_score_ws(P(a["q"]), P(a["k"]), a["n_cells"], a["pos0"], a["T"], a["Hs"], a["D"],
+                                  a["scale"], a["dead"], P(a["scores"]), a["row_stride"], P(a["ws"]),
+                                  a["ws_bytes"], P(None))
+
+
+def test_score_workspace_size():
+    # 512 bytes per row, rows rounded up to a multiple of 64
+    for T, want in [(-3, 0), (0, 0), (1, 32768), (64, 32768), (65, 65536), (1984, 1015808)]:
+        assert qsa.qsa_score_ws_bytes(T) == want, T
+
+
+@pytest.mark.parametrize("kw", [dict(ws=None), dict(ws_bytes=64 * 512 - 1), dict(ws_bytes=0),
+                                dict(ws=FAKE + 8), dict(T=65, n_cells=100, row_stride=75)])
+def test_score_ws_rejects_bad_workspaces_on_host(kw):
+    assert score_ws(**kw) == qsa.QSA_ERR_ARG
+    assert qsa.qsa_last_error().startswith("qsa_score_ws")
 
 
 def test_binding_refuses_host_tensors():

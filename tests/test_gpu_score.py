@@ -4,6 +4,7 @@ import math
 import numpy as np
 import pytest
 
+import sparse_selection_attention_amd as qsa
 from sparse_selection_attention_amd import synth
 
 import oracle
@@ -43,6 +44,44 @@ def test_ragged_row_tiles_in_both_workgroup_orders(T, pos0, Hs, extra):
     sc = synth.score_case(T=T, pos0=pos0, Hs=Hs, row_stride=pos0 + T + extra, seed=T + 7 * pos0, scale=0.6)
     print("score ragged T=%d pos0=%d worst err/A %g" % (T, pos0, check_score_case(sc, n_sample=24, seed=T)),
           flush=True)
+
+
+# (T, pos0, Hs, whether the first pass runs): it runs where q is 4 MB or more
+# and every XCD reads all of q (the run-major order of long contexts); near the
+# start of a sequence (row-major order), with small q or one head it does not,
+# and the workspace keeps its contents
+WS_SHAPES = [(1984, 30000, 12, True), (1984, 8192, 12, True), (700, 30000, 16, True), (2100, 5000, 4, True),
+             (600, 30000, 14, True), (1984, 0, 12, False), (777, 13, 16, False), (1000, 0, 3, False),
+             (96, 30000, 12, False), (1984, 30000, 1, False), (17, 5, 2, False), (1, 0, 1, False)]
+
+
+@pytest.mark.parametrize("T,pos0,Hs,prepared", WS_SHAPES)
+def test_workspace_path_gives_the_same_bits(T, pos0, Hs, prepared):
+    """qsa_score_ws: scores, tails and untouched cells are qsa_score's bit for
+    bit, and the workspace is written exactly where the first pass runs."""
+    import torch
+    sc = synth.score_case(T=T, pos0=pos0, Hs=Hs, row_stride=pos0 + T + 5, seed=11 * T + pos0, scale=0.8, dead=-3.5)
+    ws = torch.full((qsa.qsa_score_ws_bytes(T),), 0xA5, dtype=torch.uint8, device="cuda")
+    a = run_score(sc)
+    b = run_score(sc, workspace=ws)
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+    assert bool((ws != 0xA5).any()) == prepared
+
+
+def test_workspace_path_against_the_oracle():
+    sc = synth.score_case(T=1984, pos0=30000, Hs=12)
+    print("score_ws pos0=30000 worst err/A %g" % check_score_case(sc, n_sample=8, workspace=True), flush=True)
+
+
+def test_workspace_reused_across_calls():
+    """One workspace for two calls in a row that both take the first pass, the
+    second with fewer rows (a ragged last row tile): each call's scores are
+    those of qsa_score."""
+    import torch
+    ws = torch.full((qsa.qsa_score_ws_bytes(1984),), 0x5A, dtype=torch.uint8, device="cuda")
+    for T, pos0, Hs in [(1984, 30000, 12), (700, 30000, 16)]:
+        sc = synth.score_case(T=T, pos0=pos0, Hs=Hs, seed=T + 1)
+        assert np.array_equal(run_score(sc, workspace=ws).view(np.uint32), run_score(sc).view(np.uint32)), T
 
 def test_integer_scores_are_exact():
     T, pos0, Hs = 100, 30, 4
