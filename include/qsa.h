@@ -221,9 +221,10 @@ QSA_API int64_t qsa_score_ws_bytes(int32_t T);
  * leaves the workspace untouched.
  *
  * workspace  device memory of ws_bytes >= qsa_score_ws_bytes(T) bytes,
- *            16-byte aligned, owned by the caller; its contents are
- *            overwritten and mean nothing to the caller afterwards. Calls that
- *            share a workspace must be ordered (one stream, or synchronised).
+ *            16-byte aligned, owned by the caller, overlapping neither q, k
+ *            nor scores; its contents are overwritten and mean nothing to the
+ *            caller afterwards. Calls that share a workspace must be ordered
+ *            (one stream, or synchronised).
  * The other arguments, their layouts and the errors are those of qsa_score;
  * a NULL, short or misaligned workspace returns QSA_ERR_ARG before anything
  * is enqueued.
