@@ -41,10 +41,13 @@
 // could not be waited for without waiting for them too). Tiles wholly beyond
 // the last causal cell of their rows end the walk (such tiles hold no tail
 // either, since the tail never crosses a 64-cell boundary), and tiles wholly
-// inside every row's causal range are stored without per-cell tests. Scores
-// are written with nontemporal stores: a row of scores is written once and
-// read by a later kernel, so it streams past the caches instead of evicting
-// the K rows that the other workgroups are still reading.
+// inside every row's causal range are stored without per-cell tests. Where
+// every row starts 64-byte aligned (row_stride a multiple of 16), scores are
+// written with nontemporal stores: a row of scores is written once and read by
+// a later kernel, so it streams past the caches instead of evicting the K rows
+// that the other workgroups are still reading. Rows that start inside a
+// 64-byte segment have segments that two store instructions share; cached
+// stores let L2 join them, which nontemporal stores would not.
 // Workgroups are ordered so that each XCD (workgroup id mod 8) walks a
 // contiguous range of column runs, and the K rows one XCD reads stay within
 // its own L2; where that leaves the XCDs unbalanced (rows of very different
@@ -202,7 +205,20 @@ __device__ inline void stage_k(uint8_t *buf, const floatx4 (&kreg)[4], int tid)
     }
 }
 
-template <bool kPrepared>
+// A score store: nontemporal where every row starts 64-byte aligned (each
+// store instruction then writes whole 64-byte segments that nothing else
+// touches), cached otherwise, so that L2 joins the pieces of segments that
+// straddle two instructions' rows before they go to memory.
+template <bool kNT>
+__device__ inline void put(float v, float *p)
+{
+    if constexpr (kNT)
+        __builtin_nontemporal_store(v, p);
+    else
+        *p = v;
+}
+
+template <bool kPrepared, bool kNT>
 __global__ __launch_bounds__(kScoreThreads, 4) void score_kernel(ScoreArgs a, int n_row_tiles, int run_len, int n_runs, int blocks_per_xcd,
                                                                    int by_row, const uint4 *ws)
 {
@@ -331,7 +347,7 @@ __global__ __launch_bounds__(kScoreThreads, 4) void score_kernel(ScoreArgs a, in
                 float *row = a.scores + (int64_t)(r0 + rq + 4 * j + r) * a.row_stride + c0 + cq + c16;
 #pragma unroll
                 for (int ni = 0; ni < 2; ++ni)
-                    __builtin_nontemporal_store(acc[ni][r], &row[16 * ni]);
+                    put<kNT>(acc[ni][r], &row[16 * ni]);
             }
         } else if (live) {
 #pragma unroll
@@ -348,9 +364,9 @@ __global__ __launch_bounds__(kScoreThreads, 4) void score_kernel(ScoreArgs a, in
                 for (int ni = 0; ni < 2; ++ni) {
                     const int64_t c = c0 + cq + 16 * ni + c16;
                     if (c <= p)
-                        __builtin_nontemporal_store(acc[ni][r], &row[c]);
+                        put<kNT>(acc[ni][r], &row[c]);
                     else if (c < tail_end)
-                        __builtin_nontemporal_store(a.dead, &row[c]);
+                        put<kNT>(a.dead, &row[c]);
                 }
             }
         }
@@ -404,16 +420,29 @@ hipError_t launch_score(const ScoreArgs &a, void *ws, hipStream_t stream)
     // with a small q (decode steps, one head) or in the row-major order (each
     // XCD reads an eighth of q) the extra launch costs more than it saves.
     const bool prepare = ws && !by_row && (int64_t)a.T * a.Hs * kD * 4 >= kPrepareBytes;
-    if (prepare) {
+    if (prepare)
         // one strip of operands per 16 rows of every row tile (the last tile's
         // rows past T included), so the walk's reads stay inside the workspace
         hipLaunchKernelGGL(prep_kernel, dim3(4 * n_row_tiles), dim3(256), 0, stream, a, (uint4 *)ws);
-        hipLaunchKernelGGL(score_kernel<true>, dim3(8 * per_xcd), dim3(kScoreThreads), 0, stream, a, n_row_tiles,
-                           run_len, n_runs, run_major_per_xcd, by_row, (const uint4 *)ws);
-    } else {
-        hipLaunchKernelGGL(score_kernel<false>, dim3(8 * per_xcd), dim3(kScoreThreads), 0, stream, a, n_row_tiles,
-                           run_len, n_runs, run_major_per_xcd, by_row, (const uint4 *)nullptr);
-    }
+    // Nontemporal stores where every row starts 64-byte aligned; cached where
+    // rows straddle segments, which nontemporal stores would write piecemeal
+    // (T = 1984, pos0 = 30000: 80 us aligned; with an odd row stride 213 us
+    // nontemporal against 106 us cached)
+    const bool nt = ((uintptr_t)a.scores & 63) == 0 && a.row_stride % 16 == 0;
+    const dim3 grid(8 * per_xcd), block(kScoreThreads);
+    const uint4 *wsp = prepare ? (const uint4 *)ws : nullptr;
+    if (prepare && nt)
+        hipLaunchKernelGGL((score_kernel<true, true>), grid, block, 0, stream, a, n_row_tiles, run_len, n_runs,
+                           run_major_per_xcd, by_row, wsp);
+    else if (prepare)
+        hipLaunchKernelGGL((score_kernel<true, false>), grid, block, 0, stream, a, n_row_tiles, run_len, n_runs,
+                           run_major_per_xcd, by_row, wsp);
+    else if (nt)
+        hipLaunchKernelGGL((score_kernel<false, true>), grid, block, 0, stream, a, n_row_tiles, run_len, n_runs,
+                           run_major_per_xcd, by_row, wsp);
+    else
+        hipLaunchKernelGGL((score_kernel<false, false>), grid, block, 0, stream, a, n_row_tiles, run_len, n_runs,
+                           run_major_per_xcd, by_row, wsp);
     return hipGetLastError();
 }
 
