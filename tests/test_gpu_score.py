@@ -83,6 +83,24 @@ def test_workspace_reused_across_calls():
         sc = synth.score_case(T=T, pos0=pos0, Hs=Hs, seed=T + 1)
         assert np.array_equal(run_score(sc, workspace=ws).view(np.uint32), run_score(sc).view(np.uint32)), T
 
+
+@pytest.mark.parametrize("offset", [1, 8, 16])
+def test_scores_buffer_off_the_64_byte_grid(offset):
+    """A scores pointer 4, 32 or 64 bytes past an aligned base, with an even row
+    stride: rows that do not start 64-byte aligned take cached stores (the
+    first two offsets), aligned ones nontemporal stores. The scores, tails and
+    untouched cells are those of the aligned call, bit for bit."""
+    import torch
+    sc = synth.score_case(T=700, pos0=3000, Hs=12, row_stride=3000 + 700 + 12, seed=offset, scale=0.5, dead=-2.0)
+    want = run_score(sc)
+    q, k = torch.from_numpy(sc.q).cuda(), torch.from_numpy(sc.k).cuda()
+    n = sc.T * sc.row_stride
+    buf = torch.full((n + offset,), float("nan"), dtype=torch.float32, device="cuda")
+    scores = buf[offset: offset + n].view(sc.T, sc.row_stride)
+    qsa.qsa_score(q, k, sc.pos0, float(sc.scale), float(sc.dead), scores)
+    torch.cuda.synchronize()
+    assert np.array_equal(scores.cpu().numpy().view(np.uint32), want.view(np.uint32))
+
 def test_integer_scores_are_exact():
     T, pos0, Hs = 100, 30, 4
     rng = np.random.default_rng(1)
