@@ -229,15 +229,18 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(8))) void se
     // stores them.
     uint4 *words = (uint4 *)cnt;                         // [KPT * kSelWaves] {gt lo, gt hi, eq lo, eq hi}
     {
+        // each ballot's two words go straight into lane j of the collecting
+        // registers (v_writelane, lane j an immediate). Selecting them by lane
+        // instead left the compiler holding the ballots in scalar registers,
+        // 70 of which it spilled into vector lanes.
         uint32_t glo = 0, ghi = 0, elo = 0, ehi = 0;
 #pragma unroll
         for (int j = 0; j < KPT; ++j) {
             const uint64_t bg = __ballot(key[j] > tau), be = __ballot(key[j] == tau);
-            const bool mine = lane == j;
-            glo = mine ? (uint32_t)bg : glo;
-            ghi = mine ? (uint32_t)(bg >> 32) : ghi;
-            elo = mine ? (uint32_t)be : elo;
-            ehi = mine ? (uint32_t)(be >> 32) : ehi;
+            asm volatile("v_writelane_b32 %0, %1, %2" : "+v"(glo) : "s"((uint32_t)bg), "i"(j));
+            asm volatile("v_writelane_b32 %0, %1, %2" : "+v"(ghi) : "s"((uint32_t)(bg >> 32)), "i"(j));
+            asm volatile("v_writelane_b32 %0, %1, %2" : "+v"(elo) : "s"((uint32_t)be), "i"(j));
+            asm volatile("v_writelane_b32 %0, %1, %2" : "+v"(ehi) : "s"((uint32_t)(be >> 32)), "i"(j));
         }
         if (lane < KPT)
             words[lane * kSelWaves + w] = make_uint4(glo, ghi, elo, ehi);
