@@ -38,8 +38,9 @@ def sources():
 
 
 def kernel_resources(remarks: str) -> dict:
-    """Per-kernel VGPRs, scratch bytes per lane and occupancy, parsed from the
-    compiler's kernel-resource-usage remarks."""
+    """Per-kernel VGPRs, scratch bytes per lane, occupancy and scalar registers
+    spilled into vector lanes, parsed from the compiler's kernel-resource-usage
+    remarks."""
     out, name = {}, None
     for line in remarks.splitlines():
         m = re.search(r"remark: Function Name: (\S+)", line)
@@ -47,9 +48,10 @@ def kernel_resources(remarks: str) -> dict:
             name = m.group(1)
             out[name] = {}
             continue
-        m = re.search(r"remark:\s+(VGPRs|ScratchSize \[bytes/lane\]|Occupancy \[waves/SIMD\]): (\d+)", line)
+        m = re.search(r"remark:\s+(VGPRs|ScratchSize \[bytes/lane\]|Occupancy \[waves/SIMD\]|SGPRs Spill): (\d+)", line)
         if m and name:
-            out[name][m.group(1).split()[0]] = int(m.group(2))
+            key = "SGPRSpill" if m.group(1) == "SGPRs Spill" else m.group(1).split()[0]
+            out[name][key] = int(m.group(2))
     return out
 
 
@@ -67,11 +69,13 @@ def build(verbose: bool = False) -> str:
     if not res:
         raise RuntimeError("no kernel-resource-usage remarks from %s" % HIPCC)
     # every kernel keeps its state in registers and LDS: a register spill to
-    # scratch is a build error, not a silent slowdown
-    spills = {k: v for k, v in res.items() if v.get("ScratchSize", 0) != 0}
+    # scratch is a build error, not a silent slowdown, and so is a scalar
+    # register spilled into vector lanes (each spill and reload is a VALU
+    # instruction; 70 such spills once cost the selection kernel 18%)
+    spills = {k: v for k, v in res.items() if v.get("ScratchSize", 0) != 0 or v.get("SGPRSpill", 0) != 0}
     if spills:
         os.remove(LIB + ".tmp")
-        raise RuntimeError("kernels spill to scratch: %s" % spills)
+        raise RuntimeError("kernels spill registers: %s" % spills)
     if verbose:
         for k, v in sorted(res.items()):
             print(k, v, flush=True)

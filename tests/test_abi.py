@@ -232,10 +232,15 @@ def test_build_rejects_spilling_kernels():
         "a.hip:9:1: remark: Function Name: kern_b [-Rpass-analysis=kernel-resource-usage]",
         "a.hip:9:1: remark:     VGPRs: 128 [-Rpass-analysis=kernel-resource-usage]",
         "a.hip:9:1: remark:     ScratchSize [bytes/lane]: 60 [-Rpass-analysis=kernel-resource-usage]",
+        "a.hip:17:1: remark: Function Name: kern_c [-Rpass-analysis=kernel-resource-usage]",
+        "a.hip:17:1: remark:     VGPRs: 57 [-Rpass-analysis=kernel-resource-usage]",
+        "a.hip:17:1: remark:     ScratchSize [bytes/lane]: 0 [-Rpass-analysis=kernel-resource-usage]",
+        "a.hip:17:1: remark:     SGPRs Spill: 70 [-Rpass-analysis=kernel-resource-usage]",
     ])
     res = build.kernel_resources(text)
     assert res == {"kern_a": {"VGPRs": 120, "ScratchSize": 0, "Occupancy": 4},
-                   "kern_b": {"VGPRs": 128, "ScratchSize": 60}}
+                   "kern_b": {"VGPRs": 128, "ScratchSize": 60},
+                   "kern_c": {"VGPRs": 57, "ScratchSize": 0, "SGPRSpill": 70}}
 
 
 def quant(**kw):
