@@ -425,6 +425,10 @@ __global__ __launch_bounds__(64) void attn_kernel(AttnArgs a)
     const int lb = (blockIdx.x & 7) * a.blocks_per_xcd + (blockIdx.x >> 3);
     if (lb >= a.n_blocks)
         return;
+    // a wave still issuing its reads (q, ids, K copies, V rows) goes before
+    // the waves of its SIMD that are computing, so that its requests leave
+    // early; it drops back once they are all out
+    __builtin_amdgcn_s_setprio(2);
     const int k = lb / a.T;
     const int t = lb - k * a.T;
     const WaveLds L = wave_lds(lds, 0);
@@ -441,6 +445,7 @@ __global__ __launch_bounds__(64) void attn_kernel(AttnArgs a)
     uint2 ks = make_uint2(0u, 0u), vs = make_uint2(0u, 0u);
     uint2 vraw[2][8];
     const uint64_t mask = issue_chunk(a, L, slot_id(a, t, k, lane), lane, j, c16, ks, vs, vraw);
+    __builtin_amdgcn_s_setprio(0);
     const int64_t rec = ((int64_t)t * a.C + k) * a.H;
     if (mask == 0) {                 // empty chunk: (-inf, +0), o left alone
         if (lane < a.H) {
