@@ -125,9 +125,12 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(8))) void se
     const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
         (void *)(a.scores + (int64_t)t * a.row_stride), 0, n * 4, 0x00020000);
     uint32_t key[KPT];
+    // the row's reads leave ahead of the other row's passes on this CU
+    __builtin_amdgcn_s_setprio(2);
 #pragma unroll
     for (int j = 0; j < KPT; ++j)
         key[j] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rsrc, (tid + kSelThreads * j) * 4, 0, 0);
+    __builtin_amdgcn_s_setprio(0);
 #pragma unroll
     for (int j = 0; j < KPT; ++j) {
         const int lim = n - kSelThreads * j;             // uniform: cell tid + NT j < n iff tid < lim
