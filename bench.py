@@ -683,10 +683,35 @@ def main():
                 e1.record(stream)
                 torch.cuda.synchronize()
                 row[name] = e0.elapsed_time(e1) * 1e3 / 100
+
+            # the same 100 calls captured in one HIP graph and replayed: the
+            # per-call time without the host's launch cost
+            def fused_cur():
+                qsa.qsa_attn_merge(mq, mkq, mvq, mks, mvs, mids, mc.pos0, float(mc.scale), mout)
+
+            def two_cur():
+                qsa.qsa_attn(mq, mkq, mvq, mks, mvs, mids, mc.pos0, float(mc.scale), mpart)
+                qsa.qsa_merge(mpart, mc.n_chunks, mout)
+
+            for name, fn in (("fused_graph_us", fused_cur), ("two_kernel_graph_us", two_cur)):
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g):
+                    for _ in range(100):
+                        fn()
+                g.replay()
+                torch.cuda.synchronize()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                g.replay()
+                e1.record(stream)
+                torch.cuda.synchronize()
+                row[name] = e0.elapsed_time(e1) * 1e3 / 100
+                del g
             lat["ntok_%d" % ntok] = row
         result["decode_latency"] = {
             "workload": "decode window: ntok tokens at pos0=3000, 321 cells (64 sink + 256 local + current), 12 heads, "
-                        "back-to-back calls on one stream",
+                        "back-to-back calls on one stream; *_graph_us: the same calls captured in one HIP graph "
+                        "of 100 and replayed",
             **lat,
         }
 
