@@ -40,11 +40,39 @@ using dev::xor_sum;
 typedef float f4v __attribute__((ext_vector_type(4)));
 
 constexpr int kWaves = 4;
+constexpr int kUnroll = 8;          // chunks per batch of record reads
 constexpr float kLog2e = 1.4426950408889634f;
+
+// U chunks from k0 on (indexes past the last chunk re-read it; those are not
+// added): their records are all read before the first is added, and they are
+// added in chunk order with weights exp(m_k - M)
+template <int U>
+__device__ inline void combine(const MergeArgs &a, int64_t base, int k0, float M, int l32, float &L, float4 &O)
+{
+    float mk[U], lk[U];
+    float4 ov[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int k = min(k0 + u, a.C - 1);
+        const int64_t r = base + (int64_t)k * a.H;
+        mk[u] = a.m[r];
+        lk[u] = a.l[r];
+        { f4v t4 = __builtin_nontemporal_load((const f4v *)(a.o + r * kD + 4 * l32)); ov[u] = make_float4(t4.x, t4.y, t4.z, t4.w); }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const bool use = (k0 + u < a.C) && (mk[u] != -INFINITY);
+        const float wk = __builtin_amdgcn_exp2f((mk[u] - M) * kLog2e);
+        L = use ? fmaf(wk, lk[u], L) : L;
+        O.x = use ? fmaf(wk, ov[u].x, O.x) : O.x;
+        O.y = use ? fmaf(wk, ov[u].y, O.y) : O.y;
+        O.z = use ? fmaf(wk, ov[u].z, O.z) : O.z;
+        O.w = use ? fmaf(wk, ov[u].w, O.w) : O.w;
+    }
+}
 
 __global__ __launch_bounds__(64 * kWaves) void merge_kernel(MergeArgs a)
 {
-    constexpr int kUnroll = 8;
     const int lane = threadIdx.x & 63;
     const int half = lane >> 5, l32 = lane & 31;
     const int64_t hv = ((int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6)) * 2 + half;   // (t, h) pair
@@ -73,28 +101,20 @@ __global__ __launch_bounds__(64 * kWaves) void merge_kernel(MergeArgs a)
     if (M != -INFINITY) {
         float L = 0.0f;
         float4 O = make_float4(0.f, 0.f, 0.f, 0.f);
-        for (int k0 = 0; k0 < a.C; k0 += kUnroll) {
-            float mk[kUnroll], lk[kUnroll];
-            float4 ov[kUnroll];
-#pragma unroll
-            for (int u = 0; u < kUnroll; ++u) {
-                const int k = min(k0 + u, a.C - 1);
-                const int64_t r = base + (int64_t)k * a.H;
-                mk[u] = a.m[r];
-                lk[u] = a.l[r];
-                { f4v t4 = __builtin_nontemporal_load((const f4v *)(a.o + r * kD + 4 * l32)); ov[u] = make_float4(t4.x, t4.y, t4.z, t4.w); }
-            }
-#pragma unroll
-            for (int u = 0; u < kUnroll; ++u) {
-                const bool use = (k0 + u < a.C) && (mk[u] != -INFINITY);
-                const float wk = __builtin_amdgcn_exp2f((mk[u] - M) * kLog2e);
-                L = use ? fmaf(wk, lk[u], L) : L;
-                O.x = use ? fmaf(wk, ov[u].x, O.x) : O.x;
-                O.y = use ? fmaf(wk, ov[u].y, O.y) : O.y;
-                O.z = use ? fmaf(wk, ov[u].z, O.z) : O.z;
-                O.w = use ? fmaf(wk, ov[u].w, O.w) : O.w;
-            }
-        }
+        // whole batches of kUnroll chunks, then the rest as one batch of the
+        // smallest power of two that holds it (33 chunks: 4 x 8 + 1), so that
+        // few loads re-read the last chunk
+        const int c_full = a.C - a.C % kUnroll, rest = a.C - c_full;
+        for (int k0 = 0; k0 < c_full; k0 += kUnroll)
+            combine<kUnroll>(a, base, k0, M, l32, L, O);
+        if (rest == 1)
+            combine<1>(a, base, c_full, M, l32, L, O);
+        else if (rest == 2)
+            combine<2>(a, base, c_full, M, l32, L, O);
+        else if (rest > 2 && rest <= 4)
+            combine<4>(a, base, c_full, M, l32, L, O);
+        else if (rest > 4)
+            combine<kUnroll>(a, base, c_full, M, l32, L, O);
         y = make_float4(O.x / L, O.y / L, O.z / L, O.w / L);
     }
     const int64_t orow = ((int64_t)t * a.H + h) * kD + 4 * l32;
