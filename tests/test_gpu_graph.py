@@ -1,6 +1,7 @@
 """Decode steps captured in a HIP graph (torch.cuda.CUDAGraph around the C ABI
-calls). The entry points launch kernels only (no allocation, no memset), so a
-captured step replays them. Every replay, with eager work and synchronisation
+calls): fused, two-kernel, and through the static record array. The entry
+points launch kernels only (no allocation, no memset), so a captured step
+replays them. Every replay, with eager work and synchronisation
 between replays, must give the eager output bit for bit."""
 import numpy as np
 import pytest
@@ -20,7 +21,7 @@ def _inputs(ntok):
 
 
 @pytest.mark.parametrize("ntok", [1, 8])
-@pytest.mark.parametrize("path", ["fused", "two_kernel"])
+@pytest.mark.parametrize("path", ["fused", "two_kernel", "static"])
 def test_graph_replays_match_eager(ntok, path):
     mc, (q, kq, vq, ks, vs), ids = _inputs(ntok)
     out = torch.full((ntok, mc.H, 128), float("nan"), dtype=torch.float16, device="cuda")
@@ -29,6 +30,8 @@ def test_graph_replays_match_eager(ntok, path):
     def step():
         if path == "fused":
             qsa.qsa_attn_merge(q, kq, vq, ks, vs, ids, mc.pos0, float(mc.scale), out)
+        elif path == "static":           # records in the library's static array, for callers that cannot allocate
+            qsa.qsa_split_merge_static(q, kq, vq, ks, vs, ids, mc.pos0, float(mc.scale), out)
         else:
             qsa.qsa_attn(q, kq, vq, ks, vs, ids, mc.pos0, float(mc.scale), part)
             qsa.qsa_merge(part, mc.n_chunks, out)
