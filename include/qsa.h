@@ -4,11 +4,15 @@
  * q.K scores, on AMD Instinct MI355X (gfx950).
  *
  * Every pointer argument is a DEVICE pointer to memory the caller owns. The
- * library allocates nothing, keeps no per-call state and is safe to call from
- * several host threads. Each call validates its arguments on the host, enqueues
- * its kernels on `stream` (a hipStream_t; NULL means the null stream) and
- * returns without synchronising: inputs must stay alive, and outputs must not be
- * read, until the stream has passed the call.
+ * library allocates nothing, keeps no per-call state (qsa_split_merge_static's
+ * static record array aside) and is safe to call from several host threads.
+ * Each call validates its arguments on the host, enqueues its kernels on
+ * `stream` (a hipStream_t; NULL means the null stream) and returns without
+ * synchronising: inputs must stay alive, and outputs must not be read, until
+ * the stream has passed the call. A call enqueues kernel launches only (no
+ * memset, copy or host wait), so calls made while `stream` is being captured
+ * go into the HIP graph, with the pointers and sizes of that call, and every
+ * replay repeats them.
  *
  * Status codes:
  *   QSA_OK              success (also for T == 0, which enqueues nothing)
